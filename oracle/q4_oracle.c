@@ -1,0 +1,261 @@
+/*
+ * q4_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct fp64 CPU evaluation of the weight-only
+ * 4-bit linear layer.  Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the GPU product path
+ * never calls it and shares no code, header or table with it.
+ *
+ * What it computes (each function cites the passage it follows):
+ *
+ *   out[m, n] = sum_k x[m, k] * s[g(k), n] * (q[n, k] - 8)  (+ bias[n])
+ *
+ *   - Dense linear form out[m,n] = sum_k in[m,k] * weight[n,k] (+ bias[n]):
+ *     page 2, "[ExecuTorch][WebGPU] Add optimized linear_fp32 op", Solution.
+ *   - Signed nibble, dequant(W[n,k]) = (code - 8) * scale: page 3,
+ *     "Add fp32 matmul ops (mm, bmm, linear)", stack entry #20943; page 5,
+ *     "Add linear_qcs4w op", Constraints (3).
+ *   - Flat packed weight [N, K/2], K_packed == ceil(K/2): page 3 #20945
+ *     design note ("flat [N, K/2]"); page 5, Implementation (guards).
+ *   - Nibble order: the q4gsw packer stores (odd << 4) | even, so even k sits
+ *     in the LOW nibble; the qcs4w packer stores (even << 4) | odd, so even k
+ *     sits in the HIGH nibble: page 5, Constraints (2).
+ *   - Grouped scale index (k / group_size) * padded_N + n, per-channel scale
+ *     scales[n]: page 5, Solution (Before/After vs q4gsw).
+ *
+ * Arithmetic: every dequantized weight (code - 8) * s is formed exactly in
+ * fp64 (a 4-bit integer times a 24-bit significand fits in 53 bits); the sum
+ * over k runs in ascending k in fp64, with no blocking or reordering.
+ * Threads (OpenMP) only split independent output columns n; every output is
+ * computed by one thread in the same order, so results do not depend on the
+ * thread count.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+/* ------------------------------------------------------------------ */
+/* Unpack: page 5 Constraints (2) (order), page 3 #20943 (code - 8).   */
+/* ------------------------------------------------------------------ */
+
+/* The raw 4-bit code (0..15) of weight (n, k). order 0: even k in the low
+ * nibble (q4gsw packer); order 1: even k in the high nibble (qcs4w packer). */
+static int raw_code(const uint8_t *qw, int64_t ldq, int64_t n, int64_t k,
+                    int order)
+{
+    uint8_t byte = qw[n * ldq + k / 2];
+    int k_is_even = (k % 2) == 0;
+    int low = byte & 0x0F;
+    int high = (byte >> 4) & 0x0F;
+    if (order == 0)
+        return k_is_even ? low : high;
+    return k_is_even ? high : low;
+}
+
+/* Signed value c = code - 8, in [-8, 7]. */
+static int signed_code(const uint8_t *qw, int64_t ldq, int64_t n, int64_t k,
+                       int order)
+{
+    return raw_code(qw, ldq, n, k, order) - 8;
+}
+
+/* Scale of weight (n, k): grouped s[(k / gs) * lds + n]; per-channel
+ * (gs == 0) s[n].  Page 5, Solution. */
+static float scale_of(const float *scales, int64_t lds, int64_t gs, int64_t n,
+                      int64_t k)
+{
+    if (gs == 0)
+        return scales[n];
+    return scales[(k / gs) * lds + n];
+}
+
+/* Exact fp64 dequantized weight. */
+static double weight_f64(const uint8_t *qw, int64_t ldq, const float *scales,
+                         int64_t lds, int64_t gs, int64_t n, int64_t k,
+                         int order)
+{
+    return (double)signed_code(qw, ldq, n, k, order) *
+           (double)scale_of(scales, lds, gs, n, k);
+}
+
+/* ------------------------------------------------------------------ */
+/* IEEE binary16 round-to-nearest-even, written from the format's      */
+/* definition (1 sign bit, 5 exponent bits with bias 15, 10 fraction   */
+/* bits; subnormal quantum 2^-24; largest finite 65504).               */
+/* ------------------------------------------------------------------ */
+
+/* Round a double to the nearest binary16 (ties to even) and return its bit
+ * pattern.  Only exact inputs are passed in (an fp32 value, or a 4-bit
+ * integer times a binary16 value), so there is a single rounding. */
+uint16_t q4o_rn_f16_bits(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7E00u;
+    /* 65504 + half its quantum (16) is a tie between 65504 (odd fraction)
+     * and 65536 (overflow), which resolves upward: everything >= 65520
+     * becomes infinity. */
+    if (a >= 65520.0)
+        return sign | 0x7C00u;
+    if (a < 0x1p-14) {
+        /* subnormal (or zero): value = f * 2^-24, f in [0, 1024]; f == 1024
+         * encodes the smallest normal number, 0x0400, by itself. */
+        double f = rint(a * 0x1p24); /* exact scaling; rint ties to even */
+        return sign | (uint16_t)f;
+    }
+    int e2;
+    (void)frexp(a, &e2);           /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;                /* unbiased exponent, -14..15 */
+    double quantum = ldexp(1.0, E - 10);
+    double f = rint(a / quantum);  /* in [1024, 2048] */
+    if (f == 2048.0) {
+        f = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7C00u;
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(f - 1024.0));
+}
+
+/* Value of a binary16 bit pattern, as a double. */
+double q4o_f16_value(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int E = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (E == 0x1F)
+        v = f ? NAN : INFINITY;
+    else if (E == 0)
+        v = ldexp((double)f, -24);
+    else
+        v = ldexp((double)(1024 + f), E - 25);
+    return sign ? -v : v;
+}
+
+void q4o_round_f16(const float *src, int64_t n, uint16_t *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = q4o_rn_f16_bits((double)src[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Stage references (bit-exact targets for the unpack / dequant stage) */
+/* ------------------------------------------------------------------ */
+
+/* codes[n * ldc + k] = q[n, k] - 8. */
+void q4o_unpack_codes(const uint8_t *qw, int64_t ldq, int64_t N, int64_t K,
+                      int order, int8_t *codes, int64_t ldc)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            codes[n * ldc + k] = (int8_t)signed_code(qw, ldq, n, k, order);
+}
+
+/* w[n * ldw + k] = (code - 8) * s, exact, in fp64. */
+void q4o_dequant_f64(const uint8_t *qw, int64_t ldq, const float *scales,
+                     int64_t lds, int64_t gs, int64_t N, int64_t K, int order,
+                     double *w, int64_t ldw)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            w[n * ldw + k] = weight_f64(qw, ldq, scales, lds, gs, n, k, order);
+}
+
+/* fp32 dequant: the exact product (code - 8) * s rounded once to fp32. */
+void q4o_dequant_f32(const uint8_t *qw, int64_t ldq, const float *scales,
+                     int64_t lds, int64_t gs, int64_t N, int64_t K, int order,
+                     float *w, int64_t ldw)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            w[n * ldw + k] =
+                (float)weight_f64(qw, ldq, scales, lds, gs, n, k, order);
+}
+
+/* binary16 dequant: the scale is first rounded to binary16, then the exact
+ * product (code - 8) * RN16(s) is rounded once to binary16 ("f16 dequant
+ * multiply", page 1 stack entry #20752). */
+void q4o_dequant_f16(const uint8_t *qw, int64_t ldq, const float *scales,
+                     int64_t lds, int64_t gs, int64_t N, int64_t K, int order,
+                     uint16_t *w, int64_t ldw)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double s16 = q4o_f16_value(
+                q4o_rn_f16_bits((double)scale_of(scales, lds, gs, n, k)));
+            double c = (double)signed_code(qw, ldq, n, k, order);
+            w[n * ldw + k] = q4o_rn_f16_bits(c * s16);
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* The linear layer                                                    */
+/* ------------------------------------------------------------------ */
+
+/* One output: ascending-k fp64 sum of x[m,k] * w[n,k], plus bias[n];
+ * den = sum_k |x[m,k] * w[n,k]| (the normalisation of the error metric). */
+static void one_output(const float *x, int64_t ldx, const double *wrow,
+                       const float *bias, int64_t m, int64_t n, int64_t K,
+                       double *out, double *den)
+{
+    double acc = 0.0, d = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = (double)x[m * ldx + k] * wrow[k];
+        acc += p;
+        d += fabs(p);
+    }
+    if (bias)
+        acc += (double)bias[n];
+    *out = acc;
+    *den = d;
+}
+
+/* Full output: out[m * N + n], den[m * N + n] (both [M, N], fp64). */
+void q4o_linear(const float *x, int64_t ldx, const uint8_t *qw, int64_t ldq,
+                const float *scales, int64_t lds, int64_t gs,
+                const float *bias, int64_t M, int64_t N, int64_t K, int order,
+                double *out, double *den)
+{
+#pragma omp parallel
+    {
+        double *wrow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k)
+                wrow[k] = weight_f64(qw, ldq, scales, lds, gs, n, k, order);
+            for (int64_t m = 0; m < M; ++m)
+                one_output(x, ldx, wrow, bias, m, n, K, &out[m * N + n],
+                           &den[m * N + n]);
+        }
+        free(wrow);
+    }
+}
+
+/* Sampled outputs: out[i] = result at (ms[i], ns[i]). */
+void q4o_linear_sampled(const float *x, int64_t ldx, const uint8_t *qw,
+                        int64_t ldq, const float *scales, int64_t lds,
+                        int64_t gs, const float *bias, int64_t K, int order,
+                        int64_t P, const int64_t *ms, const int64_t *ns,
+                        double *out, double *den)
+{
+#pragma omp parallel
+    {
+        double *wrow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < P; ++i) {
+            int64_t n = ns[i];
+            for (int64_t k = 0; k < K; ++k)
+                wrow[k] = weight_f64(qw, ldq, scales, lds, gs, n, k, order);
+            one_output(x, ldx, wrow, bias, ms[i], n, K, &out[i], &den[i]);
+        }
+        free(wrow);
+    }
+}
+
+int q4o_max_threads(void) { return omp_get_max_threads(); }
