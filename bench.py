@@ -1,0 +1,290 @@
+"""Benchmark of the weight-only 4-bit linear layer on one MI355X.
+
+A step is one pass of the layer over the four projections of one
+Llama-3.2-1B-shaped decoder layer (2048->2048, 2048->8192 x2, 8192->2048,
+group size 32, seeded synthetic inputs):
+  * decode (M = 1, the fp32 GEMV): the headline value, in GB/s of
+    algorithmic bytes (packed weights + scales + activations + outputs);
+  * prefill (M = 512, the binary16 MFMA GEMM): reported beside it in TFLOP/s.
+
+Inputs are resident in HBM before timing starts.  Every projection's packed
+weights and scales exist in L rotating copies (L * bytes >= 1 GiB, four times
+the 256 MiB Infinity Cache) so each step streams its weights from HBM, as a
+token does when each layer has its own weights.  Steps are captured into one
+HIP graph (L steps, one per copy) and replayed; timing uses HIP events on the
+capture stream, bracketed by synchronisation.
+
+Roofline: the dominant kernel's average duration is measured live with HIP
+events over back-to-back launches captured in a graph, and priced against
+MI355X peaks (HBM 8 TB/s; dense binary16 MFMA 2516.6 TFLOP/s).
+
+cpu_baseline: the fp64 oracle (test infrastructure) timed on this host's cores
+over a bounded sample of the same step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2516.6
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--prefill-m", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["decode", "prefill", "both"], default="both")
+    return ap.parse_args()
+
+
+class Suite:
+    """Device copies of one set of projections, and graph capture of steps."""
+
+    def __init__(self, projs, torch, b, make_inputs):
+        self.torch = torch
+        self.b = b
+        self.projs = projs
+        dev = torch.device("cuda")
+        self.step_bytes = sum(p.alg_bytes() for p in projs)
+        self.step_flops = sum(p.flops() for p in projs)
+        weight_bytes = sum(p.N * p.Kp + 4 * p.G * p.N for p in projs)
+        self.copies = max(2, -(-ROTATE_BYTES // weight_bytes))
+        self.items = []
+        for p in projs:
+            x, qw, s, bias = make_inputs(p, 0)
+            qd, sd = qw.to(dev), s.to(dev)
+            qs = [qd] + [qd.clone() for _ in range(self.copies - 1)]
+            ss = [sd] + [sd.clone() for _ in range(self.copies - 1)]
+            out = torch.empty((p.M, p.N), dtype=torch.float32, device=dev)
+            need = b.workspace_bytes(p.M, p.N, p.K, p.group_size)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+            self.items.append(dict(p=p, x=x.to(dev), qs=qs, ss=ss, out=out, ws=ws,
+                                   bias=None if bias is None else bias.to(dev)))
+        torch.cuda.synchronize()
+
+    def launch(self, i, c):
+        it = self.items[i]
+        p = it["p"]
+        self.b.linear(it["x"], it["qs"][c], it["ss"][c], it["bias"], K=p.K,
+                      group_size=p.group_size, nibble_order=p.order, out=it["out"],
+                      workspace=it["ws"])
+
+    def capture(self, body):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            body()  # warm the code objects outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        torch.cuda.synchronize()
+        return g
+
+    def step_graph(self):
+        def body():
+            for c in range(self.copies):
+                for i in range(len(self.items)):
+                    self.launch(i, c)
+        return self.capture(body)
+
+    def kernel_graph(self, i, reps):
+        def body():
+            for r in range(reps):
+                self.launch(i, r % self.copies)
+        return self.capture(body)
+
+
+def time_graph(torch, g, replays):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3  # seconds
+
+
+def measure(suite, steps, warmup, torch):
+    g = suite.step_graph()
+    per_graph = suite.copies
+    replays = max(1, -(-steps // per_graph))
+    wreps = max(1, -(-warmup // per_graph))
+    time_graph(torch, g, wreps)
+    secs = time_graph(torch, g, replays)
+    nsteps = replays * per_graph
+    return dict(steps=nsteps, warmup=wreps * per_graph, seconds=secs,
+                ms_per_step=secs / nsteps * 1e3)
+
+
+def dominant_kernel(suite, torch, reps=64):
+    """Average duration of each projection's launch (back-to-back in a graph)
+    and the projection that takes the most time per step."""
+    rows = []
+    for i, it in enumerate(suite.items):
+        g = suite.kernel_graph(i, reps)
+        time_graph(torch, g, 1)
+        secs = time_graph(torch, g, 4) / (4 * reps)
+        rows.append((i, secs))
+    # time share per step = duration of this projection
+    i_dom, t_dom = max(rows, key=lambda r: r[1])
+    return rows, i_dom, t_dom
+
+
+def cpu_baseline(projs, budget_s, unit):
+    """The oracle, as is, over a bounded sample: whole rows of every
+    projection, a slice of the output columns, repeated within the budget."""
+    import numpy as np
+    from bit_weight_only_int4_amd.workloads import make_inputs
+    from oracle import q4_oracle as orc
+    total_bytes = total_flops = 0.0
+    secs = 0.0
+    frac = 1.0
+    data = []
+    for p in projs:
+        x, qw, s, bias = make_inputs(p, 0)
+        data.append((p, x.numpy(), qw.numpy(), s.numpy(),
+                     None if bias is None else bias.numpy()))
+    # one calibration pass over 1/64 of the columns, then size the sample
+    def run(f):
+        nonlocal total_bytes, total_flops, secs
+        for p, x, qw, s, bias in data:
+            ncols = max(1, int(p.N * f))
+            q_s = np.ascontiguousarray(qw[:ncols])
+            s_s = np.ascontiguousarray(s[:ncols] if p.group_size == 0 else s[:, :ncols])
+            b_s = None if bias is None else np.ascontiguousarray(bias[:ncols])
+            t0 = time.perf_counter()
+            orc.linear(x, q_s, s_s, b_s, K=p.K, group_size=p.group_size, order=p.order)
+            secs += time.perf_counter() - t0
+            share = ncols / p.N
+            total_bytes += p.alg_bytes() * share
+            total_flops += p.flops() * share
+    run(1.0 / 64)
+    est_full = secs * 64
+    frac = min(1.0, budget_s / max(est_full, 1e-9))
+    total_bytes = total_flops = secs = 0.0
+    run(frac)
+    value = total_bytes / secs / 1e9 if unit == "GB/s" else total_flops / secs / 1e12
+    return dict(value=round(value, 6), unit=unit, cores=orc.max_threads(), kind="oracle",
+                sample=f"fp64 oracle over the first {frac * 100:.2f}% of output columns "
+                       f"of each of the {len(projs)} projections (whole K, all M rows), "
+                       f"{secs:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this layer has no "
+              "multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from bit_weight_only_int4_amd import q4linear as b
+    from bit_weight_only_int4_amd.workloads import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    b.lib()  # fail loudly if the HIP library is missing
+
+    result = {}
+    dec_projs = CONFIGS["decode_1b"]
+    pre_projs = [p.with_m(args.prefill_m) for p in dec_projs]
+
+    if args.only in ("decode", "both"):
+        print(f"[bench] decode: {len(dec_projs)} projections", file=sys.stderr, flush=True)
+        dec = Suite(dec_projs, torch, b, make_inputs)
+        m = measure(dec, args.steps, args.warmup, torch)
+        rows, i_dom, t_dom = dominant_kernel(dec, torch)
+        p_dom = dec_projs[i_dom]
+        ach = p_dom.alg_bytes() / t_dom / 1e9
+        result["decode"] = dict(
+            m=m, step_bytes=dec.step_bytes, copies=dec.copies,
+            per_proj=[(dec_projs[i].name, round(t * 1e6, 3),
+                       round(dec_projs[i].alg_bytes() / t / 1e9, 1)) for i, t in rows],
+            roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                          kernel=f"gemv_f32 ({p_dom.name})",
+                          avg_launch_us=round(t_dom * 1e6, 3)))
+        print(f"[bench] decode done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
+        del dec
+        torch.cuda.empty_cache()
+
+    if args.only in ("prefill", "both"):
+        print(f"[bench] prefill M={args.prefill_m}", file=sys.stderr, flush=True)
+        pre = Suite(pre_projs, torch, b, make_inputs)
+        m = measure(pre, max(8, args.steps // 8), max(4, args.warmup // 8), torch)
+        rows, i_dom, t_dom = dominant_kernel(pre, torch, reps=16)
+        p_dom = pre_projs[i_dom]
+        ach = p_dom.flops() / t_dom / 1e12
+        result["prefill"] = dict(
+            m=m, step_flops=pre.step_flops, copies=pre.copies,
+            per_proj=[(pre_projs[i].name, round(t * 1e6, 3),
+                       round(pre_projs[i].flops() / t / 1e12, 2)) for i, t in rows],
+            roofline=dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
+                          unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                          traffic=None, kernel=f"gemm_f16 ({p_dom.name})",
+                          avg_launch_us=round(t_dom * 1e6, 3)))
+        print(f"[bench] prefill done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
+        del pre
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline and "decode" in result:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(dec_projs, args.cpu_seconds, "GB/s")
+
+    line = {"metric": "q4 linear: prefill TFLOP/s (M=512) + decode GEMV HBM GB/s, "
+                      "% of MI355X peak"}
+    if "decode" in result:
+        d = result["decode"]
+        gbs = d["step_bytes"] / (d["m"]["ms_per_step"] / 1e3) / 1e9
+        line.update({
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": d["m"]["steps"], "warmup": d["m"]["warmup"],
+            "ms_per_step": round(d["m"]["ms_per_step"], 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "decode_1b: M=1, Llama-3.2-1B q/gate/up/down "
+                                   "projections (2048x2048, 2048x8192 x2, 8192x2048), "
+                                   "group_size 32, fp32 activations N(0,1), "
+                                   "scales U[0.005,0.02], seed 0",
+                       "rotating_weight_copies": d["copies"],
+                       "alg_bytes_per_step": d["step_bytes"]},
+            "roofline": d["roofline"],
+            "per_projection_us_gbs": d["per_proj"],
+        })
+    if "prefill" in result:
+        pf = result["prefill"]
+        tf = pf["step_flops"] / (pf["m"]["ms_per_step"] / 1e3) / 1e12
+        line["prefill"] = {
+            "value": round(tf, 2), "unit": "TFLOP/s", "dtype": "f16 operands, f32 accumulate",
+            "ms_per_step": round(pf["m"]["ms_per_step"], 6), "steps": pf["m"]["steps"],
+            "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "config": {"workload": f"prefill_1b: M={args.prefill_m}, same four projections",
+                       "rotating_weight_copies": pf["copies"]},
+            "roofline": pf["roofline"],
+            "per_projection_us_tflops": pf["per_proj"],
+        }
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

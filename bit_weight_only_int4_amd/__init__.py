@@ -1,0 +1,12 @@
+"""Weight-only 4-bit linear layer for AMD MI355X (gfx950).
+
+    out[m, n] = sum_k x[m, k] * s[g(k), n] * (q[n, k] - 8)  (+ bias[n])
+
+The layer runs in hand-written HIP kernels behind the C ABI of
+``include/q4linear.h``: an fp32 streaming GEMV for M == 1 (decode) and a
+binary16 MFMA GEMM with fp32 accumulation for M > 1 (prefill).  This package
+is the thin ctypes binding (``q4linear``), the in-tree build (``build``) and
+the seeded synthetic workloads (``workloads``).
+"""
+from .q4linear import (Q4Error, dequant, library_path, lib, linear,  # noqa: F401
+                       unpack_codes, workspace_bytes)

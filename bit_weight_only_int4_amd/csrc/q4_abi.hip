@@ -1,0 +1,189 @@
+// q4_abi.hip -- the C ABI (include/q4linear.h): argument checks, regime
+// selection and launches on the caller's stream.
+//
+// Regime (page 1, stack entry #20730: M > 1 prefill GEMM; page 4: M = 1 decode
+// GEMV): Q4_MATH_AUTO runs the fp32 GEMV for M == 1 and the binary16 MFMA
+// GEMM for M > 1.  There is no fall-back ladder: each request runs the kernel
+// its math names, with ragged shapes handled inside the kernel.
+//
+// Every check runs before anything is queued (page 2, Implementation: throw
+// "before any allocation"; page 5, Implementation: "all fail-loud").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4_kernels.h"
+#include "q4linear.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t rows, int64_t pitch, int64_t width, int64_t elem) {
+  if (!p || rows <= 0 || width <= 0) return Range{0, 0};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)(((rows - 1) * pitch + width) * elem)};
+}
+
+bool overlap(Range a, Range b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// sizes representable in the kernels' index arithmetic
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+int32_t resolve_math(int32_t math, int64_t M) {
+  if (math == Q4_MATH_AUTO) return M == 1 ? Q4_MATH_F32 : Q4_MATH_F16;
+  return math;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+const char* q4_status_str(q4_status st) {
+  switch (st) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_INVALID_ARG: return "invalid argument";
+    case Q4_ERR_ALIAS: return "output overlaps an input";
+    case Q4_ERR_WORKSPACE: return "workspace missing or too small";
+    case Q4_ERR_UNSUPPORTED: return "unsupported request";
+    case Q4_ERR_DEVICE: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t q4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size,
+                                 int32_t math) {
+  if (M <= 0 || N <= 0 || K <= 0 || group_size < 0 || M >= kMaxDim || N >= kMaxDim ||
+      K >= kMaxDim)
+    return 0;
+  const int32_t m = resolve_math(math, M);
+  if (m == Q4_MATH_F32) return q4::gemv_workspace_bytes(M, N, K, group_size);
+  if (m == Q4_MATH_F16) return q4::gemm_workspace_bytes(M, N, K, group_size);
+  return 0;
+}
+
+q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
+                    const float* scales, int64_t lds, int64_t group_size, const float* bias,
+                    float* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                    int32_t nibble_order, int32_t math, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t* path_out) {
+  if (path_out) *path_out = Q4_PATH_NONE;
+  // ---- scalar checks ----
+  if (M < 0 || N < 0 || K <= 0 || group_size < 0) return Q4_ERR_INVALID_ARG;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return Q4_ERR_INVALID_ARG;
+  if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
+    return Q4_ERR_INVALID_ARG;
+  if (math != Q4_MATH_AUTO && math != Q4_MATH_F32 && math != Q4_MATH_F16)
+    return Q4_ERR_INVALID_ARG;
+  const int64_t Kp = (K + 1) / 2;
+  const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
+  if (ldx < K || ldq < Kp || ldo < N) return Q4_ERR_INVALID_ARG;
+  if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return Q4_OK;
+  // ---- pointer checks ----
+  if (!x || !qw || !scales || !out) return Q4_ERR_INVALID_ARG;
+  if (!aligned(x, 4) || !aligned(scales, 4) || !aligned(out, 4) ||
+      (bias && !aligned(bias, 4)))
+    return Q4_ERR_INVALID_ARG;
+  const Range r_out = span(out, M, ldo, N, 4);
+  const Range r_x = span(x, M, ldx, K, 4);
+  const Range r_q = span(qw, N, ldq, Kp, 1);
+  const Range r_s = group_size == 0 ? span(scales, 1, N, N, 4) : span(scales, G, lds, N, 4);
+  const Range r_b = span(bias, 1, N, N, 4);
+  if (overlap(r_out, r_x) || overlap(r_out, r_q) || overlap(r_out, r_s) ||
+      overlap(r_out, r_b))
+    return Q4_ERR_ALIAS;
+  const int32_t m = resolve_math(math, M);
+  const size_t need = q4_linear_workspace_bytes(M, N, K, group_size, m);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return Q4_ERR_WORKSPACE;
+    const Range r_w{reinterpret_cast<uintptr_t>(workspace),
+                    reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(r_w, r_out) || overlap(r_w, r_x) || overlap(r_w, r_q) ||
+        overlap(r_w, r_s) || overlap(r_w, r_b))
+      return Q4_ERR_ALIAS;
+  }
+  // 16-byte weight loads need dword-aligned rows; otherwise bytes are read
+  // one at a time
+  const bool qa4 = aligned(qw, 4) && (ldq % 4 == 0);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (m == Q4_MATH_F32) {
+    // one activation row per grid row; grid.y is at most 65535
+    const int64_t mchunk = 65535;
+    e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += mchunk) {
+      q4::GemvParams p{};
+      const int64_t mm = (M - m0 < mchunk) ? M - m0 : mchunk;
+      p.x = x + m0 * ldx; p.ldx = ldx; p.qw = qw; p.ldq = ldq;
+      p.scales = scales; p.lds = lds; p.group_size = group_size; p.G = G;
+      p.bias = bias; p.out = out + m0 * ldo; p.ldo = ldo;
+      p.partial = reinterpret_cast<float*>(workspace);
+      p.M = mm; p.N = N; p.K = K;
+      e = q4::launch_gemv(p, nibble_order, qa4, s);
+    }
+    if (path_out) *path_out = Q4_PATH_GEMV_F32;
+  } else {
+    q4::GemmParams p{};
+    p.x = x; p.ldx = ldx; p.qw = qw; p.ldq = ldq;
+    p.scales = scales; p.lds = lds; p.group_size = group_size; p.G = G;
+    p.bias = bias; p.out = out; p.ldo = ldo;
+    p.partial = reinterpret_cast<float*>(workspace);
+    p.M = M; p.N = N; p.K = K;
+    e = q4::launch_gemm(p, nibble_order, qa4, s);
+    if (path_out) *path_out = Q4_PATH_GEMM_F16;
+  }
+  return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
+}
+
+q4_status q4_unpack_codes(const uint8_t* qw, int64_t ldq, int64_t N, int64_t K,
+                          int32_t nibble_order, int8_t* codes, int64_t ldc, void* stream) {
+  if (N < 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return Q4_ERR_INVALID_ARG;
+  if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
+    return Q4_ERR_INVALID_ARG;
+  const int64_t Kp = (K + 1) / 2;
+  if (ldq < Kp || ldc < K) return Q4_ERR_INVALID_ARG;
+  if (N == 0) return Q4_OK;
+  if (!qw || !codes) return Q4_ERR_INVALID_ARG;
+  if (overlap(span(codes, N, ldc, K, 1), span(qw, N, ldq, Kp, 1))) return Q4_ERR_ALIAS;
+  const hipError_t e = q4::launch_unpack_codes(qw, ldq, N, K, nibble_order, codes, ldc,
+                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
+}
+
+q4_status q4_dequant(const uint8_t* qw, int64_t ldq, const float* scales, int64_t lds,
+                     int64_t group_size, int64_t N, int64_t K, int32_t nibble_order,
+                     int32_t dtype, void* w, int64_t ldw, void* stream) {
+  if (N < 0 || K <= 0 || group_size < 0 || N >= kMaxDim || K >= kMaxDim)
+    return Q4_ERR_INVALID_ARG;
+  if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
+    return Q4_ERR_INVALID_ARG;
+  if (dtype != Q4_DTYPE_F32 && dtype != Q4_DTYPE_F16) return Q4_ERR_INVALID_ARG;
+  const int64_t Kp = (K + 1) / 2;
+  const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
+  if (ldq < Kp || ldw < K) return Q4_ERR_INVALID_ARG;
+  if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
+  if (N == 0) return Q4_OK;
+  if (!qw || !scales || !w) return Q4_ERR_INVALID_ARG;
+  const int64_t esz = dtype == Q4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(scales, 4) || !aligned(w, (uintptr_t)esz)) return Q4_ERR_INVALID_ARG;
+  const Range r_w = span(w, N, ldw, K, esz);
+  const Range r_s = group_size == 0 ? span(scales, 1, N, N, 4) : span(scales, G, lds, N, 4);
+  if (overlap(r_w, span(qw, N, ldq, Kp, 1)) || overlap(r_w, r_s)) return Q4_ERR_ALIAS;
+  const hipError_t e = q4::launch_dequant(qw, ldq, scales, lds, group_size, N, K,
+                                          nibble_order, dtype, w, ldw,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
+}
+
+}  // extern "C"

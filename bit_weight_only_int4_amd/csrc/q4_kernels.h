@@ -1,0 +1,88 @@
+// q4_kernels.h -- host-side interface between the C ABI (q4_abi.hip) and the
+// kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "q4linear.h"
+
+namespace q4 {
+
+struct GemvParams {
+  const float* x;
+  int64_t ldx;
+  const uint8_t* qw;
+  int64_t ldq;
+  const float* scales;
+  int64_t lds;
+  int64_t group_size;  // 0 = per-channel
+  int64_t G;           // number of scale rows (1 for per-channel)
+  const float* bias;
+  float* out;
+  int64_t ldo;
+  float* partial;      // split-K workspace [split][M][N] (split > 1)
+  int64_t M, N, K;
+  int64_t k_per_split; // filled by launch_gemv
+  int32_t rows_per_block;
+  int32_t split;
+};
+
+struct GemvPlan {
+  int cfg;
+  int split;
+  int64_t k_per_split;
+  int rows_per_block;
+  int64_t blocks_n;
+};
+
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
+hipError_t launch_gemv(const GemvParams& p, int order, bool qa4, hipStream_t s);
+
+struct GemmParams {
+  const float* x;
+  int64_t ldx;
+  const uint8_t* qw;
+  int64_t ldq;
+  const float* scales;
+  int64_t lds;
+  int64_t group_size;  // 0 = per-channel
+  int64_t G;
+  const float* bias;
+  float* out;
+  int64_t ldo;
+  float* partial;      // split-K workspace [split][M][N] (split > 1)
+  int64_t M, N, K;
+  int64_t k_per_split; // multiple of the K step, filled by launch_gemm
+  int32_t split;
+  int32_t tiles_m, tiles_n;
+};
+
+struct GemmPlan {
+  int cfg;
+  int split;
+  int64_t k_per_split;
+  int tiles_m, tiles_n;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
+hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, hipStream_t s);
+
+// stage exports
+hipError_t launch_unpack_codes(const uint8_t* qw, int64_t ldq, int64_t N,
+                               int64_t K, int order, int8_t* codes,
+                               int64_t ldc, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* qw, int64_t ldq, const float* scales,
+                          int64_t lds, int64_t group_size, int64_t N,
+                          int64_t K, int order, int dtype, void* w,
+                          int64_t ldw, hipStream_t s);
+
+__global__ void splitk_reduce_kernel(const float* __restrict__ partial,
+                                     const float* __restrict__ bias,
+                                     float* __restrict__ out, int64_t ldo,
+                                     int64_t M, int64_t N, int split);
+
+}  // namespace q4

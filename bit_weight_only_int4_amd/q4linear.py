@@ -1,0 +1,159 @@
+"""Python binding of the C ABI in ``include/q4linear.h`` (ctypes).
+
+Argument marshalling only: tensors are checked, ``out`` and the workspace are
+allocated with torch, and every step of the layer runs in the HIP library on
+torch's current stream.  If the library is not built the first call raises;
+there is no CPU fallback.
+"""
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+Q4_OK = 0
+STATUS = {0: "ok", 1: "invalid argument", 2: "output overlaps an input",
+          3: "workspace missing or too small", 4: "unsupported request",
+          5: "HIP launch error"}
+ORDERS = {"low_first": 0, "high_first": 1}
+MATHS = {"auto": 0, "f32": 1, "f16": 2}
+PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16"}
+DTYPES = {torch.float32: 0, torch.float16: 1}
+
+# exported symbols of include/q4linear.h
+SYMBOLS = ("q4_linear", "q4_linear_workspace_bytes", "q4_unpack_codes",
+           "q4_dequant", "q4_status_str", "q4_abi_version")
+
+_lib = None
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is not built; run "
+            "`python -c 'import __graft_entry__ as g; g.build()'` first")
+    L = ctypes.CDLL(path)
+    P, I, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.q4_linear.argtypes = [P, I, P, I, P, I, I, P, P, I, I, I, I, I32, I32, P, SZ, P, P]
+    L.q4_linear.restype = I32
+    L.q4_linear_workspace_bytes.argtypes = [I, I, I, I, I32]
+    L.q4_linear_workspace_bytes.restype = SZ
+    L.q4_unpack_codes.argtypes = [P, I, I, I, I32, P, I, P]
+    L.q4_unpack_codes.restype = I32
+    L.q4_dequant.argtypes = [P, I, P, I, I, I, I, I32, I32, P, I, P]
+    L.q4_dequant.restype = I32
+    L.q4_status_str.argtypes = [I32]
+    L.q4_status_str.restype = ctypes.c_char_p
+    L.q4_abi_version.argtypes = []
+    L.q4_abi_version.restype = I32
+    _lib = L
+    return L
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _rows(t: torch.Tensor, name: str, dtype) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit stride along its rows")
+    return t.stride(0) if t.size(0) > 1 else max(t.size(1), t.stride(0))
+
+
+def workspace_bytes(M: int, N: int, K: int, group_size: int, math: str = "auto") -> int:
+    return int(lib().q4_linear_workspace_bytes(M, N, K, group_size, MATHS[math]))
+
+
+def linear(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
+           bias: Optional[torch.Tensor] = None, *, K: Optional[int] = None,
+           group_size: int, nibble_order: str = "low_first", math: str = "auto",
+           out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, return_path: bool = False):
+    """out[m, n] = sum_k x[m, k] * s[g(k), n] * (q[n, k] - 8) (+ bias[n]).
+
+    x [M, K] float32; qw [N, ceil(K/2)] uint8; scales [ceil(K/gs), N] float32
+    (group_size > 0) or [N] (group_size == 0); bias [N] float32 or None.
+    Row strides of x, qw, scales and out are passed through as pitches.
+    """
+    K = x.size(1) if K is None else K
+    ldx = _rows(x, "x", torch.float32)
+    ldq = _rows(qw, "qw", torch.uint8)
+    M, N = x.size(0), qw.size(0)
+    if group_size == 0:
+        if scales.dim() != 1 or scales.stride(0) != 1 or not scales.is_cuda:
+            raise ValueError("per-channel scales must be a contiguous 1-D device tensor")
+        if scales.dtype != torch.float32:
+            raise ValueError("scales must be float32")
+        lds = N
+    else:
+        lds = _rows(scales, "scales", torch.float32)
+    if bias is not None:
+        if not bias.is_cuda or bias.dtype != torch.float32 or bias.dim() != 1 \
+                or bias.stride(0) != 1:
+            raise ValueError("bias must be a contiguous float32 device vector")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ldo = _rows(out, "out", torch.float32) if M > 0 and N > 0 else max(N, 1)
+    need = workspace_bytes(M, N, K, group_size, math) if M > 0 and N > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    path = ctypes.c_int32(0)
+    st = lib().q4_linear(_ptr(x), ldx, _ptr(qw), ldq, _ptr(scales), lds, group_size,
+                         _ptr(bias), _ptr(out), ldo, M, N, K, ORDERS[nibble_order],
+                         MATHS[math], _ptr(workspace), ws_bytes, _stream(),
+                         ctypes.byref(path))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_linear")
+    return (out, PATHS[path.value]) if return_path else out
+
+
+def unpack_codes(qw: torch.Tensor, K: int, nibble_order: str = "low_first") -> torch.Tensor:
+    """Signed codes q - 8 as int8 [N, K]."""
+    ldq = _rows(qw, "qw", torch.uint8)
+    N = qw.size(0)
+    codes = torch.empty((N, K), dtype=torch.int8, device=qw.device)
+    st = lib().q4_unpack_codes(_ptr(qw), ldq, N, K, ORDERS[nibble_order], _ptr(codes), K,
+                               _stream())
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_unpack_codes")
+    return codes
+
+
+def dequant(qw: torch.Tensor, scales: torch.Tensor, K: int, group_size: int,
+            nibble_order: str = "low_first", dtype=torch.float32) -> torch.Tensor:
+    """Dequantized weight [N, K]: float32 RN32((q-8)*s) or float16 RN16((q-8)*RN16(s))."""
+    ldq = _rows(qw, "qw", torch.uint8)
+    N = qw.size(0)
+    lds = N if group_size == 0 else _rows(scales, "scales", torch.float32)
+    w = torch.empty((N, K), dtype=dtype, device=qw.device)
+    st = lib().q4_dequant(_ptr(qw), ldq, _ptr(scales), lds, group_size, N, K,
+                          ORDERS[nibble_order], DTYPES[dtype], _ptr(w), K, _stream())
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_dequant")
+    return w

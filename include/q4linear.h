@@ -1,0 +1,155 @@
+/*
+ * q4linear.h -- C ABI of the MI355X (gfx950) weight-only 4-bit linear layer.
+ *
+ *   out[m, n] = sum_k x[m, k] * s[g(k), n] * (q[n, k] - 8)  (+ bias[n])
+ *
+ * Operator contract (pages):
+ *   - dense linear form out[m,n] = sum_k in[m,k] * weight[n,k] (+ bias[n]),
+ *     bias optional: page 2, "[ExecuTorch][WebGPU] Add optimized linear_fp32
+ *     op", Solution and Implementation;
+ *   - dequant(W[n,k]) = (code - 8) * scale: page 3, "Add fp32 matmul ops (mm,
+ *     bmm, linear)", stack entry #20943;
+ *   - packed weight [N, K/2] with K_packed == ceil(K/2), grouped scales
+ *     indexed (k / group_size) * padded_N + n, per-channel scales [N], nibble
+ *     order of the two packers: page 5, "[ExecuTorch][WebGPU] Add linear_qcs4w
+ *     op", Solution, Implementation and Constraints (2);
+ *   - argument guards fail loudly before any work is queued: page 2,
+ *     Implementation ("throwing before any allocation"); page 5,
+ *     Implementation ("all fail-loud").
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument named x, qw, scales, bias, out, codes, w or
+ *     workspace is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or retains device memory.
+ *   - Work is queued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Results are valid once the stream reaches that point;
+ *     inputs must stay alive until then.
+ *   - Row pitches (ldx, ldq, lds, ldo, ldc, ldw) are in ELEMENTS of the
+ *     array's type (bytes for qw and codes).  Only natural element alignment
+ *     is required; any pitch >= the row width is accepted.
+ *   - All arguments are checked before anything is queued; on any non-OK
+ *     status no memory is read or written.  Errors are return codes; no C++
+ *     exception crosses this boundary.
+ *   - The library keeps no state besides its loaded code objects; calls are
+ *     thread-safe.  Results are deterministic: the same inputs on the same
+ *     path give bit-identical outputs.
+ */
+#ifndef Q4LINEAR_H
+#define Q4LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+
+typedef int32_t q4_status;
+#define Q4_OK 0
+#define Q4_ERR_INVALID_ARG 1  /* NULL pointer, negative size, K <= 0, pitch
+                                 below row width, unknown enum value */
+#define Q4_ERR_ALIAS 2        /* out overlaps an input */
+#define Q4_ERR_WORKSPACE 3    /* workspace NULL or smaller than required */
+#define Q4_ERR_UNSUPPORTED 4  /* a valid request this build does not run */
+#define Q4_ERR_DEVICE 5       /* the HIP runtime reported a launch error */
+
+/* Nibble order of the packed bytes (page 5, Constraints (2)). */
+#define Q4_ORDER_LOW_FIRST 0  /* q4gsw packer: byte = (q[odd k] << 4) | q[even k] */
+#define Q4_ORDER_HIGH_FIRST 1 /* qcs4w packer: byte = (q[even k] << 4) | q[odd k] */
+
+/* Arithmetic of q4_linear. */
+#define Q4_MATH_AUTO 0 /* M == 1: F32 GEMV; M > 1: F16 MFMA GEMM */
+#define Q4_MATH_F32 1  /* pure fp32: f32 dequant, f32 products, f32 sums */
+#define Q4_MATH_F16 2  /* binary16 operands (x and dequantized w) on MFMA,
+                          fp32 accumulation; never binary16 accumulation */
+
+/* Kernel that ran (reported through path_out). */
+#define Q4_PATH_NONE 0      /* nothing queued (M == 0 or N == 0) */
+#define Q4_PATH_GEMV_F32 1  /* streaming fp32 GEMV, activation rows 1..M */
+#define Q4_PATH_GEMM_F16 2  /* MFMA f16 x f16 -> f32 GEMM */
+
+/* Element type of q4_dequant's output. */
+#define Q4_DTYPE_F32 0
+#define Q4_DTYPE_F16 1
+
+/*
+ * q4_linear -- the layer.
+ *
+ *   x       float [M, ldx]        activations, ldx >= K
+ *   qw      uint8 [N, ldq]        packed weights, ldq >= ceil(K / 2) bytes;
+ *                                 for odd K the last byte's unused nibble is
+ *                                 ignored
+ *   scales  float                 group_size > 0: [ceil(K / group_size), lds],
+ *                                 lds >= N, scale of (n, k) at
+ *                                 (k / group_size) * lds + n (the last group
+ *                                 may be partial);
+ *                                 group_size == 0: per-channel [N], lds unused
+ *                                 (same result as group_size >= K)
+ *   bias    float [N] or NULL
+ *   out     float [M, ldo]        ldo >= N; must not overlap any input
+ *   nibble_order  Q4_ORDER_*
+ *   math          Q4_MATH_*
+ *   workspace     device scratch of at least q4_linear_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); its contents on entry
+ *                 are ignored and on exit are undefined
+ *   stream        hipStream_t or NULL
+ *   path_out      if not NULL, receives the Q4_PATH_* that was queued
+ *
+ * M == 0 or N == 0 is a valid no-op (Q4_OK, nothing queued).
+ * Precision: Q4_MATH_F32 holds max |out - exact| / sum_k |x * w| to about
+ * 1e-5 or better; Q4_MATH_F16 rounds x and w to binary16 (round to nearest
+ * even; w = RN16((q - 8) * RN16(s))) and sums in fp32, holding the same
+ * normalised error under 2e-3.  F16 operands overflow to infinity beyond
+ * 65504 (IEEE); callers with such magnitudes use Q4_MATH_F32.
+ */
+q4_status q4_linear(const float *x, int64_t ldx, const uint8_t *qw,
+                    int64_t ldq, const float *scales, int64_t lds,
+                    int64_t group_size, const float *bias, float *out,
+                    int64_t ldo, int64_t M, int64_t N, int64_t K,
+                    int32_t nibble_order, int32_t math, void *workspace,
+                    size_t workspace_bytes, void *stream, int32_t *path_out);
+
+/* Bytes of workspace q4_linear needs for these sizes and math (0 if none).
+ * Returns 0 as well for invalid sizes (q4_linear then reports the error). */
+size_t q4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                 int64_t group_size, int32_t math);
+
+/*
+ * q4_unpack_codes -- the signed nibble values, codes[n * ldc + k] =
+ * q[n, k] - 8 in [-8, 7] (page 3 #20943; page 5 Constraints (2)), for
+ * 0 <= n < N, 0 <= k < K.  codes: int8 [N, ldc], ldc >= K.  Same unpack as
+ * the layer's kernels.
+ */
+q4_status q4_unpack_codes(const uint8_t *qw, int64_t ldq, int64_t N,
+                          int64_t K, int32_t nibble_order, int8_t *codes,
+                          int64_t ldc, void *stream);
+
+/*
+ * q4_dequant -- the dequantized weight matrix w [N, ldw], ldw >= K:
+ *   Q4_DTYPE_F32: w = RN32((q - 8) * s)          (one rounding of the exact
+ *                                                 product)
+ *   Q4_DTYPE_F16: w = RN16((q - 8) * RN16(s))    (the scale rounded to
+ *                 binary16, then one rounding of the exact product; this is
+ *                 the operand the F16 layer feeds to MFMA; "f16 dequant
+ *                 multiply", page 1, stack entry #20752)
+ * scales / lds / group_size as in q4_linear.  w is float* for F32 and a
+ * binary16 (uint16_t bit pattern) array for F16.
+ */
+q4_status q4_dequant(const uint8_t *qw, int64_t ldq, const float *scales,
+                     int64_t lds, int64_t group_size, int64_t N, int64_t K,
+                     int32_t nibble_order, int32_t dtype, void *w,
+                     int64_t ldw, void *stream);
+
+/* Static description of a status code. */
+const char *q4_status_str(q4_status status);
+
+/* Q4_ABI_VERSION of the loaded library. */
+int32_t q4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4LINEAR_H */

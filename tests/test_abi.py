@@ -1,0 +1,133 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/q4linear.h declares, and rejects every invalid argument with its
+status code before queueing anything.
+
+No compute call is made here: every call either fails a check or is the
+M == 0 / N == 0 no-op, so the pointers below are never dereferenced (they
+are placeholders, distinct and far apart).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_weight_only_int4_amd import q4linear as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "q4linear.h")
+
+OK, INVALID, ALIAS, WORKSPACE = 0, 1, 2, 3
+
+X, Q, S, BIAS, OUT, WS = (0x10000000, 0x20000000, 0x30000000, 0x40000000,
+                          0x50000000, 0x60000000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(q4_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(b.SYMBOLS), names
+    L = b.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.q4_abi_version() == 1
+    for code, text in b.STATUS.items():
+        assert L.q4_status_str(code).decode() == text
+
+
+def base_args(**kw):
+    a = dict(x=X, ldx=256, qw=Q, ldq=128, scales=S, lds=128, gs=32, bias=BIAS, out=OUT,
+             ldo=128, M=4, N=128, K=256, order=0, math=0, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return a
+
+
+def call(a):
+    path = ctypes.c_int32(-1)
+    st = b.lib().q4_linear(a["x"], a["ldx"], a["qw"], a["ldq"], a["scales"], a["lds"],
+                           a["gs"], a["bias"], a["out"], a["ldo"], a["M"], a["N"], a["K"],
+                           a["order"], a["math"], a["ws"], a["ws_bytes"], a["stream"],
+                           ctypes.byref(path))
+    return st, path.value
+
+
+@pytest.mark.parametrize("field,value", [
+    ("x", None), ("qw", None), ("scales", None), ("out", None),
+    ("M", -1), ("N", -1), ("K", 0), ("K", -5), ("gs", -1),
+    ("ldx", 255), ("ldq", 127), ("lds", 127), ("ldo", 127),
+    ("order", 2), ("order", -1), ("math", 3), ("math", -1),
+    ("x", X + 2), ("out", OUT + 1), ("scales", S + 3), ("bias", BIAS + 2),
+    ("M", 1 << 31), ("N", 1 << 31), ("K", 1 << 31),
+])
+def test_invalid_arguments(field, value):
+    st, path = call(base_args(**{field: value}))
+    assert st == INVALID
+    assert path == 0
+
+
+def test_odd_k_packed_pitch():
+    # K = 255 needs ceil(255 / 2) = 128 bytes per row
+    assert call(base_args(K=255, ldq=127, ldx=255))[0] == INVALID
+    # per-channel scales do not need lds >= N
+    assert call(base_args(gs=0, lds=0, ldx=255, K=255, ldq=127))[0] == INVALID
+
+
+@pytest.mark.parametrize("out", [X, X + 4 * 100, Q + 64, S, BIAS])
+def test_output_overlapping_an_input_is_rejected(out):
+    st, _ = call(base_args(out=out))
+    assert st == ALIAS
+
+
+def test_noops_are_ok_and_queue_nothing():
+    for M, N in ((0, 128), (4, 0), (0, 0)):
+        st, path = call(base_args(M=M, N=N, x=None, qw=None, out=None, scales=None))
+        assert st == OK and path == 0
+
+
+def test_workspace_is_required_when_the_plan_splits():
+    L = b.lib()
+    # a tall-K, narrow-N decode is split over K
+    M, N, K = 1, 64, 65536
+    need = L.q4_linear_workspace_bytes(M, N, K, 32, 0)
+    assert need > 0
+    a = base_args(M=M, N=N, K=K, ldx=K, ldq=K // 2, lds=N, ldo=N)
+    assert call(a)[0] == WORKSPACE
+    a.update(ws=WS, ws_bytes=need - 4)
+    assert call(a)[0] == WORKSPACE
+    a.update(ws=OUT, ws_bytes=need)
+    assert call(a)[0] == ALIAS
+
+
+def test_workspace_query_is_zero_for_invalid_sizes():
+    L = b.lib()
+    assert L.q4_linear_workspace_bytes(-1, 10, 10, 0, 0) == 0
+    assert L.q4_linear_workspace_bytes(1, 10, 0, 0, 0) == 0
+
+
+def test_stage_exports_validate():
+    L = b.lib()
+    codes = 0x70000000
+    assert L.q4_unpack_codes(Q, 127, 16, 255, 0, codes, 255, None) == INVALID
+    assert L.q4_unpack_codes(Q, 128, 16, 255, 0, codes, 254, None) == INVALID
+    assert L.q4_unpack_codes(Q, 128, 16, 255, 3, codes, 255, None) == INVALID
+    assert L.q4_unpack_codes(Q, 128, 16, 255, 0, None, 255, None) == INVALID
+    assert L.q4_unpack_codes(Q, 128, 16, 255, 0, Q + 8, 255, None) == ALIAS
+    assert L.q4_unpack_codes(Q, 128, 0, 255, 0, codes, 255, None) == OK
+    w = 0x70000000
+    assert L.q4_dequant(Q, 128, S, 16, 32, 16, 255, 0, 2, w, 255, None) == INVALID
+    assert L.q4_dequant(Q, 128, S, 15, 32, 16, 255, 0, 0, w, 255, None) == INVALID
+    assert L.q4_dequant(Q, 128, S, 16, 32, 16, 255, 0, 1, w + 1, 255, None) == INVALID
+    assert L.q4_dequant(Q, 128, S, 16, 32, 16, 255, 0, 0, S + 4, 255, None) == ALIAS
+    assert L.q4_dequant(Q, 128, S, 16, 32, 0, 255, 0, 0, w, 255, None) == OK
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(b._build, "LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        b.lib()

@@ -1,0 +1,161 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element, on
+seeded synthetic inputs at sizes the oracle finishes in seconds (several
+tiles plus ragged tails), through the C ABI.
+
+Shapes include the pages' own test shapes (page 1: steel M=96 K=2048 N=256,
+steel_f16_edge M=70 K=1024 N=136, pwdq gs 64 and gs 8, the deep-K
+128 x 8192 x 2048 case) and the decode GEMV of page 4 at reduced N.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_weight_only_int4_amd.workloads import CONFIGS, make_inputs, small_projection
+from tests.gpu_util import check_case, need_gpu, run_gpu, oracle_full, normalised_error
+from tests.packing import pack
+
+pytestmark = pytest.mark.gpu
+
+
+def inputs(M, K, N, gs, order="low_first", bias=False, seed=0, x_dist=("normal",)):
+    p = small_projection(M, K, N, gs, order=order, has_bias=bias, x_dist=x_dist)
+    return make_inputs(p, seed)
+
+
+# ---- the tiny workload (M=4, K=256, N=128, gs 32, bias, seed 0) ----------
+@pytest.mark.parametrize("math", ["auto", "f32", "f16"])
+def test_tiny_config(math):
+    need_gpu()
+    p = CONFIGS["tiny"][0]
+    x, qw, s, bias = make_inputs(p, 0)
+    check_case(x, qw, s, bias, K=p.K, gs=p.group_size, order=p.order, math=math,
+               label="tiny")
+
+
+# ---- decode GEMV (M = 1) -------------------------------------------------
+@pytest.mark.parametrize("K", [256, 300, 512, 1000, 2007, 2008, 2048, 4096, 8192, 14336,
+                               20000])
+@pytest.mark.parametrize("gs", [0, 32, 128])
+def test_gemv_shapes(K, gs):
+    need_gpu()
+    N = 515
+    if gs and K % gs and gs > K:
+        gs = 32
+    x, qw, s, bias = inputs(1, K, N, gs, bias=(K % 2 == 0), seed=K + gs)
+    check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", label="gemv")
+
+
+@pytest.mark.parametrize("N", [1, 7, 8, 63, 257, 3000])
+@pytest.mark.parametrize("order", ["low_first", "high_first"])
+def test_gemv_ragged_n_and_order(N, order):
+    need_gpu()
+    x, qw, s, bias = inputs(1, 2008, N, 0, order=order, seed=N, x_dist=("uniform", -1, 1))
+    check_case(x, qw, s, bias, K=2008, gs=0, order=order, label="gemv-ragged")
+
+
+@pytest.mark.parametrize("gs", [8, 16, 24, 48, 100, 3])
+def test_gemv_other_group_sizes(gs):
+    need_gpu()
+    x, qw, s, bias = inputs(1, 1000, 130, gs, bias=True, seed=gs)
+    check_case(x, qw, s, bias, K=1000, gs=gs, order="low_first", label="gemv-gs")
+
+
+@pytest.mark.parametrize("M", [2, 3, 5])
+def test_f32_path_several_rows(M):
+    need_gpu()
+    x, qw, s, bias = inputs(M, 2048, 300, 32, bias=True, seed=M)
+    check_case(x, qw, s, bias, K=2048, gs=32, order="low_first", math="f32", label="f32-M")
+
+
+# ---- prefill GEMM (M > 1) ------------------------------------------------
+@pytest.mark.parametrize("M,K,N,gs", [
+    (96, 2048, 256, 32),     # page 1: steel
+    (70, 1024, 136, 32),     # page 1: steel_f16_edge (partial M and N tiles)
+    (96, 2048, 256, 64),     # page 1: pwdq_gs64
+    (96, 2048, 256, 8),      # page 1: pwdq_gs8 (group smaller than the K slice)
+    (128, 8192, 2048, 32),   # page 1: deep-K case
+    (2, 256, 128, 32), (7, 2048, 1000, 0), (64, 2048, 512, 32), (65, 2008, 3000, 0),
+    (130, 2007, 300, 32), (333, 2048, 700, 0), (256, 4096, 1024, 128),
+    (17, 300, 77, 100), (40, 520, 64, 3), (513, 1024, 260, 16),
+])
+@pytest.mark.parametrize("order", ["low_first", "high_first"])
+def test_gemm_shapes(M, K, N, gs, order):
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 0), seed=M * 7 + N,
+                            x_dist=("uniform", -1, 1))
+    check_case(x, qw, s, bias, K=K, gs=gs, order=order, label="gemm")
+
+
+@pytest.mark.parametrize("math", ["f32", "f16"])
+def test_row_pitches_and_unaligned_rows(math):
+    need_gpu()
+    M = 1 if math == "f32" else 33
+    x, qw, s, bias = inputs(M, 1002, 200, 32, bias=True, seed=5)
+    # ldq = 501 + 2 = 503 bytes: rows start at odd addresses
+    check_case(x, qw, s, bias, K=1002, gs=32, order="low_first", math=math,
+               pad=(5, 2, 3, 7), label="pitches")
+    check_case(x, qw, s, bias, K=1002, gs=32, order="low_first", math=math,
+               pad=(4, 3, 0, 1), label="pitches")
+
+
+# ---- exact special cases (bit-for-bit on every path) ---------------------
+@pytest.mark.parametrize("math,M", [("f32", 1), ("f32", 3), ("f16", 1), ("f16", 70),
+                                    ("auto", 200)])
+def test_integer_case_is_exact(math, M):
+    """x in {-2..2} and scales 2^-6: every product and partial sum is exact in
+    fp32 (and the operands exact in binary16), so all paths equal the oracle
+    bit for bit, tails included."""
+    need_gpu()
+    rng = np.random.default_rng(M)
+    K, N = 2008, 301
+    raw = rng.integers(0, 16, size=(N, K))
+    xi = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    qw = torch.from_numpy(pack(raw, "high_first", pad=15))
+    x = torch.from_numpy(xi)
+    s = torch.full(((K + 31) // 32, N), 2.0 ** -6)
+    bias = torch.from_numpy(rng.integers(-9, 10, size=N).astype(np.float32) * 2.0 ** -6)
+    out, path, guards = run_gpu(x, qw, s, bias, K=K, gs=32, order="high_first", math=math)
+    ref, _ = oracle_full(x, qw, s, bias, K=K, gs=32, order="high_first")
+    assert guards
+    assert np.array_equal(out.astype(np.float64), ref), path
+
+
+@pytest.mark.parametrize("math,M", [("auto", 1), ("auto", 9), ("f32", 4)])
+def test_all_eights_give_the_bias(math, M):
+    need_gpu()
+    K, N = 777, 333
+    x = torch.randn(M, K, generator=torch.Generator().manual_seed(3))
+    qw = torch.full((N, (K + 1) // 2), 0x88, dtype=torch.uint8)
+    s = torch.rand((K + 31) // 32, N, generator=torch.Generator().manual_seed(4))
+    bias = torch.randn(N, generator=torch.Generator().manual_seed(5))
+    out, path, guards = run_gpu(x, qw, s, bias, K=K, gs=32, order="low_first", math=math)
+    assert guards
+    assert np.array_equal(out, np.broadcast_to(bias.numpy(), (M, N))), path
+
+
+def test_results_are_deterministic():
+    need_gpu()
+    for M, K, N in ((1, 8192, 2048), (1, 65536, 64), (512, 2048, 512)):
+        x, qw, s, bias = inputs(M, K, N, 32, seed=11)
+        a, _, _ = run_gpu(x, qw, s, bias, K=K, gs=32, order="low_first")
+        c, _, _ = run_gpu(x, qw, s, bias, K=K, gs=32, order="low_first")
+        assert np.array_equal(a, c)
+
+
+def test_split_k_gemv_with_large_k():
+    """K beyond one workgroup's cover forces the split-K plan and its
+    reduce kernel."""
+    need_gpu()
+    x, qw, s, bias = inputs(1, 65536, 64, 32, bias=True, seed=2)
+    check_case(x, qw, s, bias, K=65536, gs=32, order="low_first", label="gemv-splitk")
+
+
+def test_empty_sizes_are_noops():
+    need_gpu()
+    from bit_weight_only_int4_amd import q4linear as b
+    dev = torch.device("cuda")
+    x = torch.empty(0, 64, device=dev)
+    qw = torch.zeros(16, 32, dtype=torch.uint8, device=dev)
+    s = torch.ones(2, 16, device=dev)
+    out, path = b.linear(x, qw, s, group_size=32, return_path=True)
+    assert out.shape == (0, 16) and path == "none"
