@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["decode", "prefill", "both"], default="both")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 256 MiB device-to-device copy (the reference "
+                         "kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -146,25 +149,46 @@ def dominant_kernel(suite, torch, reps=64):
     return rows, i_dom, t_dom
 
 
+def copy_calibration(torch, mib=1024, reps=8):
+    """A plain elementwise copy of known size (dst = -src, fp32): reads and
+    writes mib MiB per launch, more than the Infinity Cache holds, so its
+    byte counters measure HBM traffic of a known amount."""
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(kernel="elementwise neg (fp32)", bytes_read=n * 4, bytes_written=n * 4,
+                us=round(secs * 1e6, 2), gbs_read_plus_write=round(2 * n * 4 / secs / 1e9, 1))
+
+
 def cpu_baseline(projs, budget_s, unit):
-    """The oracle, as is, over a bounded sample: whole rows of every
-    projection, a slice of the output columns, repeated within the budget."""
+    """The oracle, as is, over a bounded sample of the step: a slice of the
+    output columns of every projection (whole K, all M rows), repeated until
+    about budget_s seconds of CPU work have run."""
     import numpy as np
     from bit_weight_only_int4_amd.workloads import make_inputs
     from oracle import q4_oracle as orc
-    total_bytes = total_flops = 0.0
-    secs = 0.0
-    frac = 1.0
     data = []
     for p in projs:
         x, qw, s, bias = make_inputs(p, 0)
         data.append((p, x.numpy(), qw.numpy(), s.numpy(),
                      None if bias is None else bias.numpy()))
-    # one calibration pass over 1/64 of the columns, then size the sample
+
     def run(f):
-        nonlocal total_bytes, total_flops, secs
+        secs = work_b = work_f = 0.0
         for p, x, qw, s, bias in data:
-            ncols = max(1, int(p.N * f))
+            ncols = max(1, int(round(p.N * f)))
             q_s = np.ascontiguousarray(qw[:ncols])
             s_s = np.ascontiguousarray(s[:ncols] if p.group_size == 0 else s[:, :ncols])
             b_s = None if bias is None else np.ascontiguousarray(bias[:ncols])
@@ -172,18 +196,25 @@ def cpu_baseline(projs, budget_s, unit):
             orc.linear(x, q_s, s_s, b_s, K=p.K, group_size=p.group_size, order=p.order)
             secs += time.perf_counter() - t0
             share = ncols / p.N
-            total_bytes += p.alg_bytes() * share
-            total_flops += p.flops() * share
-    run(1.0 / 64)
-    est_full = secs * 64
+            work_b += p.alg_bytes() * share
+            work_f += p.flops() * share
+        return secs, work_b, work_f
+
+    t_probe, _, _ = run(1.0 / 64)
+    est_full = t_probe * 64
     frac = min(1.0, budget_s / max(est_full, 1e-9))
-    total_bytes = total_flops = secs = 0.0
-    run(frac)
-    value = total_bytes / secs / 1e9 if unit == "GB/s" else total_flops / secs / 1e12
+    reps = 1 if frac < 1.0 else max(1, int(budget_s / max(est_full, 1e-9)))
+    secs = wb = wf = 0.0
+    for _ in range(reps):
+        a, b_, c = run(frac)
+        secs += a
+        wb += b_
+        wf += c
+    value = wb / secs / 1e9 if unit == "GB/s" else wf / secs / 1e12
     return dict(value=round(value, 6), unit=unit, cores=orc.max_threads(), kind="oracle",
-                sample=f"fp64 oracle over the first {frac * 100:.2f}% of output columns "
+                sample=f"fp64 oracle on the first {frac * 100:.2f}% of the output columns "
                        f"of each of the {len(projs)} projections (whole K, all M rows), "
-                       f"{secs:.1f} s")
+                       f"{reps} pass(es), {secs:.1f} s of CPU time")
 
 
 def main():
@@ -203,6 +234,9 @@ def main():
     b.lib()  # fail loudly if the HIP library is missing
 
     result = {}
+    if args.copy_calibration:
+        result["copy"] = copy_calibration(torch)
+        print(f"[bench] copy: {result['copy']}", file=sys.stderr, flush=True)
     dec_projs = CONFIGS["decode_1b"]
     pre_projs = [p.with_m(args.prefill_m) for p in dec_projs]
 
@@ -283,6 +317,8 @@ def main():
             "per_projection_us_tflops": pf["per_proj"],
         }
     line["cpu_baseline"] = cpu
+    if "copy" in result:
+        line["copy_calibration"] = result["copy"]
     print(json.dumps(line), flush=True)
 
 

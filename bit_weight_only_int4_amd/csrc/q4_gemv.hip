@@ -4,102 +4,156 @@
 // out[m, n] = sum_k x[m, k] * s[g(k), n] * (q[n, k] - 8) (+ bias[n]),
 // the weight-only 4-bit linear of page 3 (#20943) and page 5; at M = 1 each
 // token streams the whole weight once (page 4, "Kernel level").  The pages'
-// decode schedule (page 4, "Why (8, 16)": several rows per workgroup with a
+// decode schedule (page 4, "Why (8, 16)": several rows per workgroup and a
 // short reduction) is prior art; this kernel is laid out for wave64 and HBM3E:
 //
-//  * A lane owns CPL "chunks" of 32 consecutive k (16 packed bytes, read with
-//    one 128-bit load).  LPR lanes share a row, so one wave-wide load covers
-//    64/LPR rows x 16*LPR contiguous bytes; WK waves of a workgroup split K.
-//  * The lane's 32*CPL activations are loaded once and stay in registers
-//    while the workgroup walks its rows; only packed bytes and scales stream.
-//  * Unpack is branch-free: four v_and_or_b32 build binary16 (1024 + q) /
+//  * A wave owns a 2048-wide span of K: lane l holds the chunk of 32
+//    consecutive k at 32*l, so one wave-wide 128-bit load reads 1 KiB of one
+//    weight row and no two lanes of a wave read the same activations.  A
+//    workgroup has one wave per span (up to 8; longer K is split over
+//    grid.z) and R rows (8, 4 or 2: the most that still give >= 2048 waves);
+//    the spans' partial sums meet in LDS.
+//  * Each lane loads its activations, then its scales, then the R weight
+//    chunks, all before any arithmetic; vector loads retire in order, so the
+//    arithmetic of row r overlaps the arrival of the later rows.
+//  * Grouped scales are [G, N] row-major, so one row's scales lie N apart;
+//    each lane reads the scales of its chunk's group for the R consecutive
+//    rows of the workgroup, one 16-byte load per four rows.
+//  * Interior tiles (all rows < N, all chunks inside K) run without per-lane
+//    checks; only edge tiles take the guarded code.
+//  * Unpack is branch-free: v_and_or_b32 builds binary16 (1024 + q) and
 //    (64 + q), one v_pk_add_f16 per pair gives the exact c = q - 8, and
-//    v_fma_mix_f32 multiplies the binary16 c by the fp32 activation into an
-//    fp32 sum.  No binary16 rounding touches x or the product: the path is
-//    pure fp32.
-//  * Grouped scales (group_size % 32 == 0): one scale per chunk, applied to
-//    the chunk's partial sum.  Per-channel: applied once per output.  Any
-//    other group_size: per-weight RN32(c * s), then the fp32 product.
-//  * Reduction: xor-shuffles inside the LPR lanes of a row, then the WK wave
-//    partials are summed in LDS in fixed order (deterministic).
-//  * Split-K (grid.z > 1) writes fp32 partials to the workspace; a second
-//    kernel sums them in split order and adds the bias.
+//    v_fma_mix_f32 multiplies c by the fp32 activation into an fp32 sum (no
+//    binary16 rounding touches x or the products: the path is pure fp32).
+//    A chunk's partial sum is scaled once (group_size a power of two from 32
+//    to 2048), or each weight is RN32(c * s) (any other group_size);
+//    per-channel scales multiply the finished dot product.
+//  * The 64-lane sum uses DPP row operations; span waves are then added in
+//    order, so results are deterministic.  With K split over grid.z the
+//    partial sums go to the workspace and a second kernel adds them in split
+//    order.
 #include "q4_device.h"
 #include "q4_kernels.h"
 
 namespace q4 {
 namespace {
 
-constexpr int kMaxRowsPerBlock = 256;
+enum ScaleMode : int { kPerChannel = 0, kStaged = 1, kGeneric = 2 };
 
-enum ScaleMode : int { kPerChannel = 0, kGroup32 = 1, kGeneric = 2 };
 
 template <bool QA4>
 __device__ __forceinline__ void load_chunk(const uint8_t* row, int64_t byte0,
                                            int64_t row_bytes, bool full,
                                            uint32_t (&w)[4]) {
-  if (full) {
-    if (QA4) {
-      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(row + byte0);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
+  if (full && QA4) {
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(row + byte0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    return;
+  }
+  // unaligned rows, or the ragged end of a row: byte loads; bytes past the
+  // row become 0x88 (c = 0) and meet zero activations
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t v = 0;
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          v |= (uint32_t)row[byte0 + 4 * d + b] << (8 * b);
-        w[d] = v;
-      }
+    for (int b = 0; b < 4; ++b) {
+      const int64_t o = byte0 + 4 * d + b;
+      const uint32_t byte = (full || o < row_bytes) ? (uint32_t)row[o] : 0x88u;
+      v |= byte << (8 * b);
     }
-  } else {
-    // Ragged tail: bytes past the row are replaced by 0x88 (c = 0); the
-    // matching activations are zero, so they add exactly nothing.
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t o = byte0 + 4 * d + b;
-        const uint32_t byte = (o < row_bytes) ? (uint32_t)row[o] : 0x88u;
-        v |= byte << (8 * b);
-      }
-      w[d] = v;
-    }
+    w[d] = v;
   }
 }
 
-template <int LPR, int CPL, int WK, int ORDER, int SMODE, bool QA4>
-__global__ void __launch_bounds__(64 * WK)
-gemv_f32_kernel(const GemvParams p) {
-  constexpr int RPI = 64 / LPR;  // rows per wave-wide load
-  constexpr int U = 2;           // row iterations whose loads are in flight together
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int rs = lane / LPR;  // row slot of this lane
-  const int j = lane % LPR;   // position inside the row's lanes
-  const int64_t m = blockIdx.y;
-  const int z = blockIdx.z;
-  const uint32_t bx = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int64_t n0 = (int64_t)bx * p.rows_per_block;
-  const int rows_here = p.rows_per_block;
-  const int iters = rows_here / RPI;
-  const int64_t kz0 = (int64_t)z * p.k_per_split;
-  const int64_t kz1 = (kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K;
+// sum_k x * c over one 32-k chunk (four packed words), fp32 throughout
+template <int ORDER>
+__device__ __forceinline__ float chunk_dot(const uint32_t (&q)[4], const float (&x)[32],
+                                           const Magic& mg) {
+  float part[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    h2 c[4];
+    unpack_word(q[d], mg, c);
+    float a = 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      a = __builtin_fmaf((float)c[pp].x, x[8 * d + pair_k<ORDER>(pp, 0)], a);
+      a = __builtin_fmaf((float)c[pp].y, x[8 * d + pair_k<ORDER>(pp, 1)], a);
+    }
+    part[d] = a;
+  }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// same with a per-weight scale, w = RN32(c * s(k))
+template <int ORDER>
+__device__ __forceinline__ float chunk_dot_generic(const uint32_t (&q)[4], const float (&x)[32],
+                                                   const Magic& mg, const float* scol,
+                                                   int64_t lds, int64_t gs, int64_t G,
+                                                   int64_t k0, bool valid) {
+  float part[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    h2 c[4];
+    unpack_word(q[d], mg, c);
+    float a = 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ko = 8 * d + pair_k<ORDER>(pp, h);
+        int64_t g = (k0 + ko) / gs;
+        g = g < G - 1 ? g : G - 1;
+        const float s = valid ? scol[g * lds] : 0.0f;
+        const float w = (float)(h == 0 ? c[pp].x : c[pp].y) * s;
+        a = __builtin_fmaf(w, x[ko], a);
+      }
+    part[d] = a;
+  }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Sum over the 64 lanes of a wave with DPP row operations (quad swaps, half
+// row and row mirrors, then the gfx9 row broadcasts); lane 63 ends with the
+// total, which is returned wave-uniform.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_take(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_take<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_take<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_take<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_take<0x140, 0xF>(v);  // row_mirror
+  v += dpp_take<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_take<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// One wave's tile: R rows x its 2048*CPL-wide K span.  GUARD = false is the
+// interior case (every row < N, every chunk inside K): no per-lane checks.
+// Loads are issued in the order they are consumed (activations, scales,
+// then the weight rows one by one) and vector loads retire in order, so the
+// arithmetic of row r overlaps the arrival of rows r+1 .. R-1.
+template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16, bool GUARD>
+__device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_t n0,
+                                          int64_t kspan, int64_t kz1, int lane,
+                                          float (&acc)[R]) {
   const int64_t row_bytes = (p.K + 1) >> 1;
-
-  __shared__ float red[WK][kMaxRowsPerBlock];
-
-  // ---- activations of this lane's chunks, kept in registers ----
   int64_t k0[CPL];
   bool kfull[CPL], kany[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    k0[t] = kspan + 32 * (t * 64 + lane);
+    kfull[t] = !GUARD || k0[t] + 32 <= kz1;
+    kany[t] = !GUARD || k0[t] < kz1;
+  }
+  // activations of this lane's chunks
   float xr[CPL][32];
   const float* xrow = p.x + m * p.ldx;
 #pragma unroll
   for (int t = 0; t < CPL; ++t) {
-    k0[t] = kz0 + 32 * (int64_t)(wave * LPR * CPL + t * LPR + j);
-    kfull[t] = k0[t] + 32 <= kz1;
-    kany[t] = k0[t] < kz1;
     if (kfull[t]) {
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
@@ -109,91 +163,111 @@ gemv_f32_kernel(const GemvParams p) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        xr[t][i] = (k0[t] + i < kz1) ? xrow[k0[t] + i] : 0.0f;
+      for (int i = 0; i < 32; ++i) xr[t][i] = (k0[t] + i < kz1) ? xrow[k0[t] + i] : 0.0f;
     }
   }
-
+  // grouped scales: the R consecutive rows of this chunk's group, one
+  // 16-byte load per four rows when aligned
+  float sv[CPL][R];
+  if (SMODE == kStaged) {
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int64_t g = k0[t] >> p.log2_gs;
+      const float* srow = p.scales + (kany[t] ? g : 0) * p.lds + n0;
+      if (SA16 && !GUARD) {
+#pragma unroll
+        for (int r4 = 0; r4 < R; r4 += 4) {
+          const f32x4_a4 v = *reinterpret_cast<const f32x4_a4*>(srow + r4);
+          sv[t][r4 + 0] = v.x; sv[t][r4 + 1] = v.y; sv[t][r4 + 2] = v.z; sv[t][r4 + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          sv[t][r] = (kany[t] && (!GUARD || n0 + r < p.N)) ? srow[r] : 0.0f;
+      }
+    }
+  }
+  // packed weights: R rows x CPL 16-byte loads, all in flight together
+  uint32_t qv[R][CPL][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool rowok = !GUARD || n0 + r < p.N;
+    const uint8_t* qrow = p.qw + (rowok ? n0 + r : 0) * p.ldq;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      if (rowok && kany[t]) {
+        load_chunk<QA4>(qrow, k0[t] >> 1, row_bytes, kfull[t], qv[r][t]);
+      } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) qv[r][t][d] = 0x88888888u;
+      }
+    }
+  }
   const Magic mg = Magic::make();
-
-  for (int it = 0; it < iters; it += U) {
-    uint32_t qv[U][CPL][4];
-    float sv[U][CPL];
-    bool rvalid[U];
-    int64_t nrow[U];
-    // issue every load of the U row iterations before any arithmetic
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      nrow[u] = n0 + (int64_t)(it + u) * RPI + rs;
-      rvalid[u] = (it + u < iters) && (nrow[u] < p.N);
-      const uint8_t* qrow = p.qw + nrow[u] * p.ldq;
+  for (int r = 0; r < R; ++r) {
+    float a = 0.0f;
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) {
-        if (rvalid[u] && kany[t]) {
-          load_chunk<QA4>(qrow, k0[t] >> 1, row_bytes, kfull[t], qv[u][t]);
-          if (SMODE == kGroup32)
-            sv[u][t] = p.scales[(k0[t] / p.group_size) * p.lds + nrow[u]];
-        } else {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) qv[u][t][d] = 0x88888888u;
-          sv[u][t] = 0.0f;
-        }
+    for (int t = 0; t < CPL; ++t) {
+      if (SMODE == kGeneric) {
+        const int64_t n = n0 + r;
+        const bool ok = (!GUARD || n < p.N) && kany[t];
+        a += chunk_dot_generic<ORDER>(qv[r][t], xr[t], mg, p.scales + (ok ? n : 0), p.lds,
+                                      p.group_size, p.G, k0[t], ok);
+      } else if (SMODE == kStaged) {
+        a = __builtin_fmaf(sv[t][r], chunk_dot<ORDER>(qv[r][t], xr[t], mg), a);
+      } else {
+        a += chunk_dot<ORDER>(qv[r][t], xr[t], mg);
       }
     }
+    acc[r] = a;
+  }
+}
+
+// Workgroup: WK waves, one per 2048*CPL span of K, over the same R rows.
+template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16>
+__global__ void __launch_bounds__(512)
+gemv_f32_kernel(const GemvParams p) {
+  __shared__ float red[8][R];
+  constexpr int SPAN = 64 * CPL * 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int64_t m = blockIdx.y;
+  const int z = blockIdx.z;
+  const int64_t n0 = (int64_t)xcd_swizzle(blockIdx.x, gridDim.x) * R;
+  const int64_t kz0 = (int64_t)z * p.k_per_split;
+  const int64_t kz1 = (kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K;
+  const int64_t kspan = kz0 + (int64_t)wave * SPAN;
+
+  float acc[R];
+  if (n0 + R <= p.N && kspan + SPAN <= kz1)
+    gemv_tile<CPL, R, ORDER, SMODE, QA4, SA16, false>(p, m, n0, kspan, kz1, lane, acc);
+  else
+    gemv_tile<CPL, R, ORDER, SMODE, QA4, SA16, true>(p, m, n0, kspan, kz1, lane, acc);
+
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float acc = 0.0f;
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  if (nwaves > 1) {
+    if (lane == 0) {
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) {
-        float part[4];
+      for (int r = 0; r < R; ++r) red[wave][r] = acc[r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          h2 c[4];
-          unpack_word(qv[u][t][d], mg, c);
-          float a = 0.0f;
-          if (SMODE == kGeneric) {
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const int ko = 8 * d + pair_k<ORDER>(pp, h);
-                int64_t g = (k0[t] + ko) / p.group_size;
-                g = g < p.G - 1 ? g : p.G - 1;
-                const float s = (rvalid[u] && kany[t]) ? p.scales[g * p.lds + nrow[u]] : 0.0f;
-                const float w = (float)(h == 0 ? c[pp].x : c[pp].y) * s;  // RN32(c * s)
-                a = __builtin_fmaf(w, xr[t][ko], a);
-              }
-          } else {
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              a = __builtin_fmaf((float)c[pp].x, xr[t][8 * d + pair_k<ORDER>(pp, 0)], a);
-              a = __builtin_fmaf((float)c[pp].y, xr[t][8 * d + pair_k<ORDER>(pp, 1)], a);
-            }
-          }
-          part[d] = a;
-        }
-        const float chunk = (part[0] + part[1]) + (part[2] + part[3]);
-        if (SMODE == kGroup32)
-          acc = __builtin_fmaf(sv[u][t], chunk, acc);
-        else
-          acc += chunk;
-      }
-      // reduce over the LPR lanes of this row slot
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1)
-        acc += __shfl_xor(acc, off, 64);
-      if (j == 0 && (it + u) < iters)
-        red[wave][(it + u) * RPI + rs] = acc;
+    for (int r = 0; r < R; ++r) {
+      float v = red[0][r];
+      for (int w = 1; w < nwaves; ++w) v += red[w][r];
+      acc[r] = v;
     }
   }
-  __syncthreads();
-
-  for (int r = threadIdx.x; r < rows_here; r += 64 * WK) {
-    const int64_t n = n0 + r;
-    if (n >= p.N) continue;
-    float v = red[0][r];
+  // lane r of wave 0 stores row n0 + r
 #pragma unroll
-    for (int w = 1; w < WK; ++w) v += red[w][r];
+  for (int r = 0; r < R; ++r) {
+    const int64_t n = n0 + r;
+    if (lane != r || n >= p.N) continue;
+    float v = acc[r];
     if (SMODE == kPerChannel) v *= p.scales[n];
     if (p.split > 1) {
       p.partial[((int64_t)z * p.M + m) * p.N + n] = v;
@@ -219,27 +293,37 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial,
   out[m * ldo + n] = v;
 }
 
-// ---- host-side launch ----------------------------------------------------
+// ---- host-side plan and launch ---------------------------------------------
 
 namespace {
 
-template <int LPR, int CPL, int WK, int ORDER, int SMODE, bool QA4>
-hipError_t launch_t(const GemvParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_f32_kernel<LPR, CPL, WK, ORDER, SMODE, QA4>), grid,
-                     dim3(64 * WK), 0, s, p);
+int scale_mode(int64_t gs, int64_t K) {
+  if (gs == 0 || gs >= K) return kPerChannel;
+  const bool pow2 = (gs & (gs - 1)) == 0;
+  if (pow2 && gs >= 32 && gs <= 2048) return kStaged;
+  return kGeneric;
+}
+
+template <int R, int ORDER, int SMODE, bool QA4, bool SA16>
+hipError_t launch_t(const GemvParams& p, dim3 grid, int nwaves, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_f32_kernel<1, R, ORDER, SMODE, QA4, SA16>), grid, dim3(64 * nwaves),
+                     0, s, p);
   return hipGetLastError();
 }
 
-template <int LPR, int CPL, int WK>
-hipError_t launch_cfg(const GemvParams& p, dim3 grid, int order, int smode,
-                      bool qa4, hipStream_t s) {
-#define Q4_GEMV_CASE(O, S, A)                                        \
-  if (order == O && smode == S && qa4 == A)                          \
-    return launch_t<LPR, CPL, WK, O, S, A>(p, grid, s);
-  Q4_GEMV_CASE(0, 0, true) Q4_GEMV_CASE(0, 1, true) Q4_GEMV_CASE(0, 2, true)
-  Q4_GEMV_CASE(1, 0, true) Q4_GEMV_CASE(1, 1, true) Q4_GEMV_CASE(1, 2, true)
-  Q4_GEMV_CASE(0, 0, false) Q4_GEMV_CASE(0, 1, false) Q4_GEMV_CASE(0, 2, false)
-  Q4_GEMV_CASE(1, 0, false) Q4_GEMV_CASE(1, 1, false) Q4_GEMV_CASE(1, 2, false)
+template <int R>
+hipError_t launch_r(const GemvParams& p, dim3 grid, int nwaves, int order, int smode, bool qa4,
+                    bool sa16, hipStream_t s) {
+#define Q4_GEMV_CASE(O, S, A, B) \
+  if (order == O && smode == S && qa4 == A && sa16 == B) return launch_t<R, O, S, A, B>(p, grid, nwaves, s);
+  Q4_GEMV_CASE(0, 0, true, false) Q4_GEMV_CASE(0, 2, true, false)
+  Q4_GEMV_CASE(1, 0, true, false) Q4_GEMV_CASE(1, 2, true, false)
+  Q4_GEMV_CASE(0, 0, false, false) Q4_GEMV_CASE(0, 2, false, false)
+  Q4_GEMV_CASE(1, 0, false, false) Q4_GEMV_CASE(1, 2, false, false)
+  Q4_GEMV_CASE(0, 1, true, true) Q4_GEMV_CASE(0, 1, true, false)
+  Q4_GEMV_CASE(1, 1, true, true) Q4_GEMV_CASE(1, 1, true, false)
+  Q4_GEMV_CASE(0, 1, false, true) Q4_GEMV_CASE(0, 1, false, false)
+  Q4_GEMV_CASE(1, 1, false, true) Q4_GEMV_CASE(1, 1, false, false)
 #undef Q4_GEMV_CASE
   return hipErrorInvalidValue;
 }
@@ -247,30 +331,20 @@ hipError_t launch_cfg(const GemvParams& p, dim3 grid, int order, int smode,
 }  // namespace
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
-  GemvPlan pl{};
-  // lanes per row, chunks per lane and waves per workgroup, smallest cover of K
-  struct Cfg { int lpr, cpl, wk; };
-  static const Cfg cfgs[] = {{8, 1, 1}, {16, 1, 4}, {32, 1, 4}, {64, 1, 4}, {64, 2, 4}};
-  int ci = 4;
-  for (int i = 0; i < 5; ++i) {
-    const int64_t cover = (int64_t)cfgs[i].lpr * cfgs[i].cpl * cfgs[i].wk * 32;
-    if (cover >= K) { ci = i; break; }
-  }
-  pl.cfg = ci;
-  const int64_t cover = (int64_t)cfgs[ci].lpr * cfgs[ci].cpl * cfgs[ci].wk * 32;
-  pl.split = (int)((K + cover - 1) / cover);
-  pl.k_per_split = cover;
-  const int rpi = 64 / cfgs[ci].lpr;
-  // rows per workgroup: keep >= ~1024 workgroups where N allows, and at
-  // least two wave-wide loads per wave
-  int64_t rpb = rpi * 2;
-  const int64_t target_blocks = 1024;
-  while (rpb * 2 <= kMaxRowsPerBlock &&
-         ((N + rpb * 2 - 1) / (rpb * 2)) * pl.split * M >= target_blocks)
-    rpb *= 2;
-  pl.rows_per_block = (int)rpb;
-  pl.blocks_n = (N + rpb - 1) / rpb;
   (void)group_size;
+  GemvPlan pl{};
+  pl.cfg = 1;  // one chunk of 32 k per lane; a wave spans 2048 k
+  const int64_t spans = (K + 2047) / 2048;
+  pl.split = (int)((spans + 7) / 8);  // at most 8 span-waves per workgroup
+  pl.waves_k = (int)((spans + pl.split - 1) / pl.split);
+  pl.waves_r = 1;
+  pl.k_per_split = (int64_t)pl.waves_k * 2048;
+  // rows per workgroup: 8 where that still gives >= 2048 waves, else 4, 2
+  int rows = 8;
+  while (rows > 2 && ((N + rows - 1) / rows) * pl.waves_k * pl.split * M < 2048) rows /= 2;
+  pl.rows_per_wave = rows;
+  pl.rows_per_block = rows;
+  pl.blocks_n = (N + rows - 1) / rows;
   return pl;
 }
 
@@ -285,29 +359,28 @@ hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s)
   p.rows_per_block = pl.rows_per_block;
   p.k_per_split = pl.k_per_split;
   p.split = pl.split;
-  int smode;
-  if (p.group_size == 0 || p.group_size >= p.K) smode = kPerChannel;
-  else if (p.group_size % 32 == 0) smode = kGroup32;
-  else smode = kGeneric;
-  if (smode == kPerChannel && p.group_size != 0) {
-    // one group covering all of K: the scale row 0 is a per-channel vector
-    p.group_size = 0;
-  }
+  p.waves_k = pl.waves_k;
+  p.waves_r = 1;
+  const int smode = scale_mode(p.group_size, p.K);
+  if (smode == kPerChannel) p.group_size = 0;  // one group: scale row 0 per channel
+  int l2 = 0;
+  if (smode == kStaged)
+    while ((1LL << l2) < p.group_size) ++l2;
+  p.log2_gs = l2;
+  const int R = pl.rows_per_wave;
+  // four consecutive scales per 16-byte load: needs 16-byte aligned rows of
+  // the scale matrix (each row group starts at a multiple of R >= 4)
+  const bool sa16 = smode == kStaged && R >= 4 &&
+                    (reinterpret_cast<uintptr_t>(p.scales) % 16 == 0) && (p.lds % 4 == 0);
   const dim3 grid((unsigned)pl.blocks_n, (unsigned)p.M, (unsigned)pl.split);
-  hipError_t e;
-  switch (pl.cfg) {
-    case 0: e = launch_cfg<8, 1, 1>(p, grid, order, smode, qa4, s); break;
-    case 1: e = launch_cfg<16, 1, 4>(p, grid, order, smode, qa4, s); break;
-    case 2: e = launch_cfg<32, 1, 4>(p, grid, order, smode, qa4, s); break;
-    case 3: e = launch_cfg<64, 1, 4>(p, grid, order, smode, qa4, s); break;
-    default: e = launch_cfg<64, 2, 4>(p, grid, order, smode, qa4, s); break;
-  }
+  const hipError_t e =
+      R == 8   ? launch_r<8>(p, grid, pl.waves_k, order, smode, qa4, sa16, s)
+      : R == 4 ? launch_r<4>(p, grid, pl.waves_k, order, smode, qa4, sa16, s)
+               : launch_r<2>(p, grid, pl.waves_k, order, smode, qa4, sa16, s);
   if (e != hipSuccess || pl.split == 1) return e;
   const int64_t total = p.M * p.N;
-  const int threads = 256;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + threads - 1) / threads)),
-                     dim3(threads), 0, s, p.partial, p.bias, p.out, p.ldo, p.M, p.N,
-                     p.split);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     s, p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split);
   return hipGetLastError();
 }
 

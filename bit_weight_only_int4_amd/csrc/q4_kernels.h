@@ -27,10 +27,16 @@ struct GemvParams {
   int64_t k_per_split; // filled by launch_gemv
   int32_t rows_per_block;
   int32_t split;
+  int32_t log2_gs;     // power-of-two group sizes: log2(group_size)
+  int32_t waves_k;     // waves per workgroup along K (one 2048*CPL span each)
+  int32_t waves_r;     // waves per workgroup along N (R rows each)
 };
 
 struct GemvPlan {
-  int cfg;
+  int cfg;            // chunks of 32 k per lane (1 or 2)
+  int waves_k;        // waves per workgroup along K, each over 2048 * cfg k
+  int waves_r;        // waves per workgroup along N
+  int rows_per_wave;  // R
   int split;
   int64_t k_per_split;
   int rows_per_block;
