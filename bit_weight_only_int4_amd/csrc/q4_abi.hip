@@ -106,7 +106,7 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
   const size_t need = q4_linear_workspace_bytes(M, N, K, group_size, m);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
-    if (!aligned(workspace, 4)) return Q4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return Q4_ERR_WORKSPACE;
     const Range r_w{reinterpret_cast<uintptr_t>(workspace),
                     reinterpret_cast<uintptr_t>(workspace) + need};
     if (overlap(r_w, r_out) || overlap(r_w, r_x) || overlap(r_w, r_q) ||
@@ -138,9 +138,8 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
     p.x = x; p.ldx = ldx; p.qw = qw; p.ldq = ldq;
     p.scales = scales; p.lds = lds; p.group_size = group_size; p.G = G;
     p.bias = bias; p.out = out; p.ldo = ldo;
-    p.partial = reinterpret_cast<float*>(workspace);
     p.M = M; p.N = N; p.K = K;
-    e = q4::launch_gemm(p, nibble_order, qa4, s);
+    e = q4::launch_gemm(p, nibble_order, qa4, workspace, s);
     if (path_out) *path_out = Q4_PATH_GEMM_F16;
   }
   return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;

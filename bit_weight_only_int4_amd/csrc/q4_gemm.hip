@@ -5,278 +5,520 @@
 //             (+ bias[n]), summed in fp32.
 // Precision recipe: binary16 operands, fp32 accumulator, never binary16
 // accumulation (page 1, stack entry #20752, "f16 multiply / f32 accumulate");
-// every packed word and scale crosses into the chip once per tile and is
+// every packed word and scale of a tile crosses into the chip once and is
 // unpacked once (page 1, stack entry #20798, the packed-word-dequant
 // staging).  The pages' 64x64 / 256-thread WGSL tile is prior art only.
 //
-// Layout on gfx950 (wave64, v_mfma_f32_16x16x32_f16):
-//  * A workgroup (4 waves) owns a BM x (4*WN) output tile; wave w owns the
-//    columns [w*WN, (w+1)*WN) for all BM rows, so every dequantized weight is
-//    produced exactly once per tile.
-//  * K advances in steps of 128.  Activations of the step (BM x 128 fp32)
-//    are read from global memory, rounded to binary16 and written into a
-//    double-buffered LDS tile, shared by the four waves.
-//  * Weights do not pass through LDS: lane (j, b) of a wave reads the 16
-//    packed bytes holding k = 32b .. 32b+31 of column j of each 16-column
-//    subtile (one 128-bit load), unpacks them with v_and_or_b32 /
-//    v_pk_add_f16 and scales them with v_pk_mul_f16 into MFMA B fragments.
-//    Word t of those 16 bytes feeds MFMA t of the step.
-//  * The k order inside each 8-element fragment follows the nibble order of
-//    the packed word; the activation tile is stored with the same
-//    permutation, so A and B fragments pair up k for k.
-//  * Ragged M, N and K are masked in-kernel (zero activations, 0x88 bytes,
-//    predicated stores); no fall-back kernel.
-//  * Split-K (grid.z > 1) writes fp32 partials to the workspace; the shared
-//    reduce kernel sums them in split order and adds the bias.
+// Layout on gfx950 (wave64, v_mfma_f32_32x32x16_f16, which sustains close to
+// the dense binary16 peak where the 16x16x32 shape reaches about half):
+//  * A pre-pass rounds the activations to binary16 once (RN16), in the k
+//    order described below, zero-padded to whole tiles, into the workspace;
+//    the GEMM then reads 2 bytes per activation instead of 4 on every
+//    column tile that reuses it, and needs no row or K masks for them.
+//  * A workgroup owns a 128 x 256 output tile (8 waves, 2 x 4) when such
+//    tiles alone fill the CUs, else 128 x 128 (4 waves, 2 x 2); each wave
+//    a 64 x 64 sub-tile of four 32x32 MFMA blocks.
+//  * K advances 64 per step.  Each step the workgroup stages in LDS the
+//    activation tile (128 x 64 binary16, copied) and the weight tile: 256
+//    or 128 columns x 64 k of packed bytes, one 16-byte load per thread, unpacked
+//    with v_and_or_b32 / v_pk_add_f16 and scaled with v_pk_mul_f16 once per
+//    tile and shared by both wave rows.  The LDS tiles are double-buffered
+//    and the global loads run three steps ahead in a register ring, so
+//    their latency hides behind the MFMAs of the steps in between.
+//  * Inside every 8-element group the k order follows the nibble order of
+//    the packed word (pairs (i, i+4)); the activations are stored with the
+//    same permutation, so A and B fragments pair up k for k.
+//  * Interior column tiles take code without bounds checks; ragged N and K
+//    are masked in the edge code (0x88 bytes, predicated stores); no
+//    fall-back kernel.
+//  * Split-K (grid.z > 1), only for deep K on few tiles, writes fp32
+//    partials to the workspace; the shared reduce kernel sums them in split
+//    order and adds the bias.
 #include "q4_device.h"
 #include "q4_kernels.h"
 
 namespace q4 {
 namespace {
 
-constexpr int KS = 128;        // k per pipeline step
-constexpr int APITCH = KS + 8; // LDS row pitch in halves (bank-conflict pad)
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int KS = 64;          // k per pipeline step
+constexpr int PITCH = KS + 8;   // LDS row pitch in halves
+constexpr int BM = 128;         // output rows per workgroup
+constexpr int DEPTH = 3;        // steps of global loads in flight
 
 enum ScaleMode : int { kPerChannel = 0, kGroup32 = 1, kGroup8 = 2, kGeneric = 3 };
 
-template <int BM, int WN, int ORDER, int SMODE, bool QA4>
+// x16[r * kp + k] = RN16(x[r, k']) for r < mp, k < kp, where inside each
+// group of 8 the k' follow the nibble order of the packed words (pairs
+// (i, i + 4)); rows >= M and k >= K are zero.  One thread per 8 elements.
+template <int ORDER>
 __global__ void __launch_bounds__(256)
+x16_kernel(const float* __restrict__ x, int64_t ldx, int64_t M, int64_t K,
+           _Float16* __restrict__ x16, int64_t mp, int64_t kp) {
+  const int64_t groups = kp / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= mp * groups) return;
+  const int64_t r = idx / groups, k0 = 8 * (idx % groups);
+  const float* src = x + r * ldx + k0;
+  float v[8];
+  if (r < M && k0 + 8 <= K) {
+    const f32x4_a4 a = *reinterpret_cast<const f32x4_a4*>(src);
+    const f32x4_a4 b = *reinterpret_cast<const f32x4_a4*>(src + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (r < M && k0 + i < K) ? src[i] : 0.0f;
+  }
+  h8 h;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) h[sl] = (_Float16)v[pair_k<ORDER>(sl >> 1, sl & 1)];
+  *reinterpret_cast<h8*>(x16 + r * kp + k0) = h;
+}
+
+// BN = 128 or 256 output columns per workgroup; NT = 2 * BN threads: waves
+// 2 (rows) x BN/64 (columns), each 64 x 64; thread t dequantizes half a
+// step of column t / 2.
+template <int BN, int ORDER, int SMODE, bool QA4>
+struct Gemm {
+  static constexpr int NT = 2 * BN;
+  static constexpr int WAVES_N = BN / 64;
+  static constexpr int WM = 64, WN = 64;  // per wave
+  static constexpr int MI = 2, NI = 2;    // 32x32 blocks per wave
+  static constexpr int AU = BM * KS / 8 / NT;  // 16-byte activation pieces per thread
+
+  struct Stage {
+    u32x4 a[AU];  // 16-byte pieces of the binary16 activation tile
+    uint32_t q[4];
+    float s[4];
+  };
+
+  const GemmParams& p;
+  int tid, lane, wm, wn;
+  int kz1;                  // end of this split's K range
+  int row_bytes;
+  int bcol;                 // this thread's weight column in the tile
+  int bhalf;                // which 32-k half of each step it dequantizes
+  bool nvalid;
+  // streaming state, advanced by one step after every load
+  const _Float16* pa[AU];   // the thread's activation pieces
+  const uint8_t* pq;        // the thread's 16 packed bytes
+  const float* pscol;       // scales + column
+  int kc;                   // first k of the thread's chunk
+  h2 s16c;                  // per-channel scale, rounded once
+
+  __device__ Gemm(const GemmParams& p_, int64_t m0, int64_t n0, int kz0, int kz1_)
+      : p(p_), kz1(kz1_) {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wm = (tid >> 6) / WAVES_N;
+    wn = (tid >> 6) % WAVES_N;
+    row_bytes = (int)((p.K + 1) >> 1);
+    bcol = tid >> 1;
+    bhalf = tid & 1;
+    const int64_t ncol = n0 + bcol;
+    nvalid = ncol < p.N;
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const int unit = tid + u * NT;
+      pa[u] = p.x16 + (m0 + (unit >> 3)) * p.x16_pitch + kz0 + 8 * (unit & 7);
+    }
+    kc = kz0 + 32 * bhalf;
+    pq = p.qw + (nvalid ? ncol : 0) * p.ldq + (kc >> 1);
+    pscol = p.scales + (nvalid ? ncol : 0);
+    if (SMODE == kPerChannel) s16c = splat_f16(nvalid ? *pscol : 0.0f);
+  }
+
+  __device__ __forceinline__ int group_of(int k) const {
+    return p.log2_gs >= 0 ? (k >> p.log2_gs) : k / (int)p.group_size;
+  }
+
+  template <bool GUARD>
+  __device__ __forceinline__ void load(Stage& st) {
+    // activations: already binary16, zero-padded to the tile grid
+#pragma unroll
+    for (int u = 0; u < AU; ++u) st.a[u] = *reinterpret_cast<const u32x4*>(pa[u]);
+    const bool any = !GUARD || (nvalid && kc < kz1);
+    const bool full = !GUARD || kc + 32 <= kz1;
+    if (any) {
+      if (full && QA4) {
+        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(pq);
+        st.q[0] = v.x; st.q[1] = v.y; st.q[2] = v.z; st.q[3] = v.w;
+      } else {
+        const int byte0 = kc >> 1;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            // bytes past the row hold no k < K; their activations are 0
+            const bool in = full || byte0 + 4 * d + b < row_bytes;
+            w |= (in ? (uint32_t)pq[4 * d + b] : 0x88u) << (8 * b);
+          }
+          st.q[d] = w;
+        }
+      }
+      if (SMODE == kGroup32) {
+        st.s[0] = pscol[(int64_t)group_of(kc) * p.lds];
+      } else if (SMODE == kGroup8) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          int g = group_of(kc + 8 * d);
+          g = g < (int)p.G - 1 ? g : (int)p.G - 1;
+          st.s[d] = pscol[(int64_t)g * p.lds];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) { st.q[d] = 0x88888888u; st.s[d] = 0.0f; }
+    }
+#pragma unroll
+    for (int u = 0; u < AU; ++u) pa[u] += KS;
+    pq += KS / 2;
+    kc += KS;
+  }
+
+  __device__ __forceinline__ void store(int kb, const Stage& st, _Float16* As,
+                                        _Float16* Bs, const Magic& mg) const {
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const int unit = tid + u * NT;
+      const int r = unit >> 3, c = unit & 7;
+      *reinterpret_cast<u32x4*>(&As[r * PITCH + 8 * c]) = st.a[u];
+    }
+    const int kcs = kb + 32 * bhalf;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      h2 c[4];
+      unpack_word(st.q[d], mg, c);
+      h2 w[4];
+      if (SMODE == kGeneric) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            int g = (kcs + 8 * d + pair_k<ORDER>(pp, hh)) / (int)p.group_size;
+            g = g < (int)p.G - 1 ? g : (int)p.G - 1;
+            const _Float16 s16 = (_Float16)(nvalid ? pscol[(int64_t)g * p.lds] : 0.0f);
+            const _Float16 cc = hh == 0 ? c[pp].x : c[pp].y;
+            if (hh == 0) w[pp].x = cc * s16; else w[pp].y = cc * s16;
+          }
+      } else {
+        const h2 s16 = SMODE == kPerChannel ? s16c
+                       : SMODE == kGroup32  ? splat_f16(st.s[0])
+                                            : splat_f16(st.s[d]);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) w[pp] = dequant_pair_f16(c[pp], s16);
+      }
+      const h8 hw = {w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
+      *reinterpret_cast<h8*>(&Bs[bcol * PITCH + 32 * bhalf + 8 * d]) = hw;
+    }
+  }
+
+  __device__ __forceinline__ void compute(const _Float16* As, const _Float16* Bs,
+                                          f16v (&acc)[MI][NI]) const {
+    const int li = lane & 31, lb = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      h8 a[MI], b[NI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        a[i] = *reinterpret_cast<const h8*>(&As[(wm * WM + i * 32 + li) * PITCH + 32 * lb + 8 * t]);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        b[j] = *reinterpret_cast<const h8*>(&Bs[(wn * WN + j * 32 + li) * PITCH + 32 * lb + 8 * t]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+template <int BN, int ORDER, int SMODE, bool QA4>
+__global__ void __launch_bounds__(2 * BN)
 gemm_f16_kernel(const GemmParams p) {
-  constexpr int NSUB = WN / 16;   // 16-column subtiles per wave
-  constexpr int MSUB = BM / 16;   // 16-row subtiles
-  constexpr int BN = 4 * WN;
-  constexpr int UNITS = BM * KS / 8;          // 8-element activation units per step
-  constexpr int UPT = UNITS / 256;            // units per thread
-  static_assert(UNITS % 256 == 0, "tile");
-
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * APITCH];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int lj = lane & 15;   // column (B) / row (A) inside a 16-subtile
-  const int lb = lane >> 4;   // k block of the lane
+  using G = Gemm<BN, ORDER, SMODE, QA4>;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * PITCH];
 
   const uint32_t tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tm = (int)(tile % (uint32_t)p.tiles_m);
   const int tn = (int)(tile / (uint32_t)p.tiles_m);
   const int64_t m0 = (int64_t)tm * BM;
-  const int64_t nw0 = (int64_t)tn * BN + (int64_t)wave * WN;
+  const int64_t n0 = (int64_t)tn * BN;
   const int z = blockIdx.z;
   const int64_t kz0 = (int64_t)z * p.k_per_split;
   const int64_t kz1 = (kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K;
-  const int64_t row_bytes = (p.K + 1) >> 1;
   const int nsteps = (int)((kz1 - kz0 + KS - 1) / KS);
+  const bool inner_n = n0 + BN <= p.N;
 
-  // ---- per-lane B columns ----
-  int64_t ncol[NSUB];
-  bool nvalid[NSUB];
-  const uint8_t* qrow[NSUB];
-  h2 s16c[NSUB];  // per-channel scale, rounded once
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    ncol[s] = nw0 + s * 16 + lj;
-    nvalid[s] = ncol[s] < p.N;
-    qrow[s] = p.qw + (nvalid[s] ? ncol[s] : 0) * p.ldq;
-    if (SMODE == kPerChannel)
-      s16c[s] = splat_f16(nvalid[s] ? p.scales[ncol[s]] : 0.0f);
-  }
-
-  // ---- activation staging: global fp32 -> registers ----
-  float4 xa[UPT][2];
-  auto load_a = [&](int step) {
-    const int64_t kb = kz0 + (int64_t)step * KS;
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * 256;
-      const int r = unit / (KS / 8);
-      const int g8 = unit % (KS / 8);
-      const int64_t row = m0 + r;
-      const int64_t k = kb + 8 * g8;
-      const float* src = p.x + row * p.ldx + k;
-      if (row < p.M && k + 8 <= kz1) {
-        const f32x4_a4 v0 = *reinterpret_cast<const f32x4_a4*>(src);
-        const f32x4_a4 v1 = *reinterpret_cast<const f32x4_a4*>(src + 4);
-        xa[u][0] = make_float4(v0.x, v0.y, v0.z, v0.w);
-        xa[u][1] = make_float4(v1.x, v1.y, v1.z, v1.w);
-      } else {
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          t[i] = (row < p.M && k + i < kz1) ? src[i] : 0.0f;
-        xa[u][0] = make_float4(t[0], t[1], t[2], t[3]);
-        xa[u][1] = make_float4(t[4], t[5], t[6], t[7]);
-      }
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * 256;
-      const int r = unit / (KS / 8);
-      const int g8 = unit % (KS / 8);
-      const float v[8] = {xa[u][0].x, xa[u][0].y, xa[u][0].z, xa[u][0].w,
-                          xa[u][1].x, xa[u][1].y, xa[u][1].z, xa[u][1].w};
-      h8 h;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl)
-        h[sl] = (_Float16)v[pair_k<ORDER>(sl >> 1, sl & 1)];  // RN16, permuted
-      *reinterpret_cast<h8*>(&As[buf][r * APITCH + 8 * g8]) = h;
-    }
-  };
-
-  // ---- weight chunks: 16 packed bytes per lane per subtile ----
-  uint32_t qc[NSUB][4];
-  float sc[NSUB][4];  // kGroup32: [s][0]; kGroup8: per word
-  auto load_b = [&](int step) {
-    const int64_t kb = kz0 + (int64_t)step * KS + 32 * lb;
-    const bool full = kb + 32 <= kz1;
-    const bool any = kb < kz1;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      if (nvalid[s] && any) {
-        const uint8_t* row = qrow[s];
-        const int64_t byte0 = kb >> 1;
-        if (full && QA4) {
-          const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(row + byte0);
-          qc[s][0] = v.x; qc[s][1] = v.y; qc[s][2] = v.z; qc[s][3] = v.w;
-        } else {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int64_t o = byte0 + 4 * d + b;
-              // bytes past the row hold no k < K; their activations are 0
-              const bool in = full || o < row_bytes;
-              w |= (in ? (uint32_t)row[o] : 0x88u) << (8 * b);
-            }
-            qc[s][d] = w;
-          }
-        }
-        if (SMODE == kGroup32) {
-          sc[s][0] = p.scales[(kb / p.group_size) * p.lds + ncol[s]];
-        } else if (SMODE == kGroup8) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            int64_t g = (kb + 8 * d) / p.group_size;
-            g = g < p.G - 1 ? g : p.G - 1;
-            sc[s][d] = p.scales[g * p.lds + ncol[s]];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) { qc[s][d] = 0x88888888u; sc[s][d] = 0.0f; }
-      }
-    }
-  };
-
-  f4 acc[MSUB][NSUB];
-#pragma unroll
-  for (int i = 0; i < MSUB; ++i)
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[i][s] = f4{0.f, 0.f, 0.f, 0.f};
-
+  G g(p, m0, n0, (int)kz0, (int)kz1);
   const Magic mg = Magic::make();
+  f16v acc[G::MI][G::NI];
+#pragma unroll
+  for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if (nsteps > 0) {
-    load_a(0);
-    load_b(0);
-    store_a(0);
-  }
+  // Register ring of DEPTH staged steps: the global loads of step s+DEPTH
+  // are issued while step s computes, so each load has DEPTH-1 steps of
+  // MFMA work to arrive before its step is written to LDS.
+  typename G::Stage st[DEPTH];
+  // loads are issued in step order; g advances its pointers after each
+  auto load_step = [&](int step, typename G::Stage& dst) {
+    const int64_t kb = kz0 + (int64_t)step * KS;
+    if (inner_n && kb + KS <= kz1) g.template load<false>(dst);
+    else g.template load<true>(dst);
+  };
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (i < nsteps) load_step(i, st[i]);
+  if (nsteps > 0) g.store((int)kz0, st[0], As[0], Bs[0], mg);
   __syncthreads();
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    uint32_t qcur[NSUB][4];
-    float scur[NSUB][4];
+  for (int step0 = 0; step0 < nsteps; step0 += DEPTH) {
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) { qcur[s][d] = qc[s][d]; scur[s][d] = sc[s][d]; }
-    const int64_t kb_lane = kz0 + (int64_t)step * KS + 32 * lb;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      load_a(step + 1);
-      load_b(step + 1);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h8 bf[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        h2 c[4];
-        unpack_word(qcur[s][t], mg, c);
-        h2 w[4];
-        if (SMODE == kGeneric) {
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              int64_t g = (kb_lane + 8 * t + pair_k<ORDER>(pp, h)) / p.group_size;
-              g = g < p.G - 1 ? g : p.G - 1;
-              const float sv = nvalid[s] ? p.scales[g * p.lds + ncol[s]] : 0.0f;
-              const _Float16 s16 = (_Float16)sv;
-              const _Float16 cc = h == 0 ? c[pp].x : c[pp].y;
-              if (h == 0) w[pp].x = cc * s16; else w[pp].y = cc * s16;
-            }
-        } else {
-          h2 s16;
-          if (SMODE == kPerChannel) s16 = s16c[s];
-          else if (SMODE == kGroup32) s16 = splat_f16(scur[s][0]);
-          else s16 = splat_f16(scur[s][t]);
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) w[pp] = dequant_pair_f16(c[pp], s16);
-        }
-        bf[s] = h8{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
-      }
-#pragma unroll
-      for (int i = 0; i < MSUB; ++i) {
-        const h8 af = *reinterpret_cast<const h8*>(
-            &As[buf][(i * 16 + lj) * APITCH + 32 * lb + 8 * t]);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[s], acc[i][s], 0, 0, 0);
+    for (int i = 0; i < DEPTH; ++i) {
+      const int step = step0 + i;
+      if (step < nsteps) {
+        const int buf = step & 1;
+        // slot i held this step; it is in LDS now, so it takes step + DEPTH
+        if (step + DEPTH < nsteps) load_step(step + DEPTH, st[i]);
+        g.compute(As[buf], Bs[buf], acc);
+        if (step + 1 < nsteps)
+          g.store((int)kz0 + (step + 1) * KS, st[(i + 1) % DEPTH], As[buf ^ 1], Bs[buf ^ 1],
+                  mg);
+        __syncthreads();
       }
     }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: D[4*lb + r][lj] of each 16x16 subtile ----
-  float bcol[NSUB];
+  // ---- epilogue: lane l, element v of a 32x32 block holds
+  //      row 8*(v/4) + 4*(l/32) + v%4, column l%32 ----
+  const int lane = threadIdx.x & 63;
+  const int wm = (threadIdx.x >> 6) / G::WAVES_N, wn = (threadIdx.x >> 6) % G::WAVES_N;
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-    bcol[s] = (p.split == 1 && p.bias && nvalid[s]) ? p.bias[ncol[s]] : 0.0f;
+  for (int j = 0; j < G::NI; ++j) {
+    const int64_t col = n0 + wn * G::WN + j * 32 + (lane & 31);
+    if (col >= p.N) continue;
+    const float bcol = (p.split == 1 && p.bias) ? p.bias[col] : 0.0f;
 #pragma unroll
-  for (int i = 0; i < MSUB; ++i)
+    for (int i = 0; i < G::MI; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + i * 16 + 4 * lb + r;
-      if (row >= p.M) continue;
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        if (!nvalid[s]) continue;
-        const float v = acc[i][s][r];
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * G::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row >= p.M) continue;
         if (p.split > 1)
-          p.partial[((int64_t)z * p.M + row) * p.N + ncol[s]] = v;
+          p.partial[((int64_t)z * p.M + row) * p.N + col] = acc[i][j][v];
         else
-          p.out[row * p.ldo + ncol[s]] = v + bcol[s];
+          p.out[row * p.ldo + col] = acc[i][j][v] + bcol;
       }
-    }
+  }
 }
 
-template <int BM, int WN, int ORDER, int SMODE, bool QA4>
-hipError_t launch_t(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_f16_kernel<BM, WN, ORDER, SMODE, QA4>), grid, dim3(256), 0, s, p);
+// ---------------------------------------------------------------------------
+// Fast path: power-of-two group sizes >= 32 or per-channel scales, K a
+// multiple of 32, dword-aligned weight rows, and every offset below 2^32
+// bytes.  The main loop has
+// no branches: each thread holds 32-bit offsets into three buffer resources
+// (binary16 activations, packed weights, scales), advanced by the step's k.
+// Reads past the end of a resource return 0, and the activations are zero
+// beyond M and K, so steps and columns past the edges add nothing; only the
+// epilogue stores are predicated.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+template <int BN, int ORDER, bool PERCH>
+__global__ void __launch_bounds__(2 * BN)
+gemm_fast_kernel(const GemmParams p) {
+  constexpr int NT = 2 * BN;
+  constexpr int WAVES_N = BN / 64;
+  constexpr int AU = BM * KS / 8 / NT;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * PITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wm = (tid >> 6) / WAVES_N, wn = (tid >> 6) % WAVES_N;
+  const uint32_t tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int tm = (int)(tile % (uint32_t)p.tiles_m);
+  const int tn = (int)(tile / (uint32_t)p.tiles_m);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
+  const int z = blockIdx.z;
+  const int kz0 = (int)((int64_t)z * p.k_per_split);
+  const int kz1 = (int)((kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K);
+  const int nsteps = (kz1 - kz0 + KS - 1) / KS;
+
+  // buffer resources and per-thread offsets
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(p.x16 + m0 * p.x16_pitch, (uint64_t)BM * p.x16_pitch * 2);
+  uint32_t va[AU];
+#pragma unroll
+  for (int u = 0; u < AU; ++u) {
+    const int unit = tid + u * NT;
+    va[u] = (uint32_t)(((unit >> 3) * p.x16_pitch + 8 * (unit & 7)) * 2);
+  }
+  const int bcol = tid >> 1, bhalf = tid & 1;
+  const int64_t ncol = n0 + bcol;
+  // resource sizes are the exact extents the caller guarantees: the last
+  // weight row holds ceil(K/2) bytes, the last scale row N floats
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(p.qw, (uint64_t)(p.N - 1) * p.ldq + (uint64_t)((p.K + 1) >> 1));
+  const uint32_t vq = (uint32_t)(ncol * p.ldq + 16 * bhalf);  // past the end when ncol >= N
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vs = 0;
+  h2 s16c = {(_Float16)0.0f, (_Float16)0.0f};
+  if (PERCH) {
+    s16c = splat_f16(ncol < p.N ? p.scales[ncol] : 0.0f);
+  } else {
+    rs = make_rsrc(p.scales, ((uint64_t)(p.G - 1) * p.lds + (uint64_t)p.N) * 4);
+    // with 32-wide groups the two halves of a step sit in consecutive groups
+    vs = (uint32_t)((ncol + (p.log2_gs == 5 ? bhalf * p.lds : 0)) * 4);
+  }
+
+  struct Stage {
+    u32x4 a[AU];
+    u32x4 q;
+    float s;
+  };
+  // The step offset goes into the per-lane offset (not the scalar one),
+  // because the hardware range check covers only the per-lane offset: every
+  // byte read is then checked against the resource size, and reads past it
+  // return 0.
+  auto load = [&](int step, Stage& st) {
+    const uint32_t kb = (uint32_t)(kz0 + step * KS);
+#pragma unroll
+    for (int u = 0; u < AU; ++u)
+      st.a[u] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, va[u] + 2 * kb, 0, 0));
+    st.q = __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rq, vq + (kb >> 1), 0, 0));
+    if (!PERCH)
+      st.s = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(
+                     rs, vs + (uint32_t)((kb >> p.log2_gs) * (uint64_t)p.lds * 4), 0, 0));
+  };
+  const Magic mg = Magic::make();
+  auto store = [&](const Stage& st, _Float16* A, _Float16* B) {
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const int unit = tid + u * NT;
+      *reinterpret_cast<u32x4*>(&A[(unit >> 3) * PITCH + 8 * (unit & 7)]) = st.a[u];
+    }
+    const h2 s16 = PERCH ? s16c : splat_f16(st.s);
+    const uint32_t qw4[4] = {st.q.x, st.q.y, st.q.z, st.q.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      h2 c[4];
+      unpack_word(qw4[d], mg, c);
+      h2 w[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) w[pp] = dequant_pair_f16(c[pp], s16);
+      const h8 hw = {w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
+      *reinterpret_cast<h8*>(&B[bcol * PITCH + 32 * bhalf + 8 * d]) = hw;
+    }
+  };
+  f16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int li = lane & 31, lb = lane >> 5;
+  auto compute = [&](const _Float16* A, const _Float16* B) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      h8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const h8*>(&A[(wm * 64 + i * 32 + li) * PITCH + 32 * lb + 8 * t]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const h8*>(&B[(wn * 64 + j * 32 + li) * PITCH + 32 * lb + 8 * t]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Two staged steps in registers, two LDS buffers: at step s the loads of
+  // step s+2 are issued, step s is computed from LDS, and step s+1 is
+  // written to the other LDS buffer.  Loads and stores past the last step
+  // only touch data that is never computed.
+  Stage r0, r1;
+  load(0, r0);
+  load(1, r1);
+  store(r0, As[0], Bs[0]);
+  __syncthreads();
+  int step = 0;
+  for (; step + 2 <= nsteps; step += 2) {
+    load(step + 2, r0);
+    compute(As[0], Bs[0]);
+    store(r1, As[1], Bs[1]);
+    __syncthreads();
+    load(step + 3, r1);
+    compute(As[1], Bs[1]);
+    store(r0, As[0], Bs[0]);
+    __syncthreads();
+  }
+  if (step < nsteps) compute(As[0], Bs[0]);
+
+  // epilogue: lane l, element v of a 32x32 block holds row
+  // 8*(v/4) + 4*(l/32) + v%4 and column l%32
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t col = n0 + wn * 64 + j * 32 + li;
+    if (col >= p.N) continue;
+    const float bcolv = (p.split == 1 && p.bias) ? p.bias[col] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3);
+        if (row >= p.M) continue;
+        if (p.split > 1)
+          p.partial[((int64_t)z * p.M + row) * p.N + col] = acc[i][j][v];
+        else
+          p.out[row * p.ldo + col] = acc[i][j][v] + bcolv;
+      }
+  }
+}
+
+template <int BN, int ORDER, bool PERCH>
+hipError_t launch_fast_t(const GemmParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_fast_kernel<BN, ORDER, PERCH>), grid, dim3(2 * BN), 0, s, p);
   return hipGetLastError();
 }
 
-template <int BM, int WN>
+template <int BN>
+hipError_t launch_fast(const GemmParams& p, dim3 grid, int order, bool perch, hipStream_t s) {
+  if (order == 0) return perch ? launch_fast_t<BN, 0, true>(p, grid, s) : launch_fast_t<BN, 0, false>(p, grid, s);
+  return perch ? launch_fast_t<BN, 1, true>(p, grid, s) : launch_fast_t<BN, 1, false>(p, grid, s);
+}
+
+template <int BN, int ORDER, int SMODE, bool QA4>
+hipError_t launch_t(const GemmParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_f16_kernel<BN, ORDER, SMODE, QA4>), grid, dim3(2 * BN), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BN>
 hipError_t launch_cfg(const GemmParams& p, dim3 grid, int order, int smode, bool qa4,
                       hipStream_t s) {
 #define Q4_GEMM_CASE(O, S, A) \
-  if (order == O && smode == S && qa4 == A) return launch_t<BM, WN, O, S, A>(p, grid, s);
+  if (order == O && smode == S && qa4 == A) return launch_t<BN, O, S, A>(p, grid, s);
   Q4_GEMM_CASE(0, 0, true) Q4_GEMM_CASE(0, 1, true) Q4_GEMM_CASE(0, 2, true) Q4_GEMM_CASE(0, 3, true)
   Q4_GEMM_CASE(1, 0, true) Q4_GEMM_CASE(1, 1, true) Q4_GEMM_CASE(1, 2, true) Q4_GEMM_CASE(1, 3, true)
   Q4_GEMM_CASE(0, 0, false) Q4_GEMM_CASE(0, 1, false) Q4_GEMM_CASE(0, 2, false) Q4_GEMM_CASE(0, 3, false)
@@ -285,42 +527,53 @@ hipError_t launch_cfg(const GemmParams& p, dim3 grid, int order, int smode, bool
   return hipErrorInvalidValue;
 }
 
-struct Cfg { int bm, wn; };
-constexpr Cfg kCfgs[] = {{64, 32}, {128, 64}};
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   (void)group_size;
   GemmPlan pl{};
-  pl.cfg = (M <= 64) ? 0 : 1;
-  const int bm = kCfgs[pl.cfg].bm, bn = 4 * kCfgs[pl.cfg].wn;
-  pl.tiles_m = (int)((M + bm - 1) / bm);
-  pl.tiles_n = (int)((N + bn - 1) / bn);
-  const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+  const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t ksteps = (K + KS - 1) / KS;
-  // split K while the grid is under ~one workgroup per CU and every split
-  // keeps at least 4 steps
+  // 128 x 256 tiles when they alone fill the CUs, else 128 x 128
+  pl.cfg = tiles_m * ((N + 255) / 256) >= 256 ? 256 : 128;
+  pl.tiles_m = (int)tiles_m;
+  pl.tiles_n = (int)((N + pl.cfg - 1) / pl.cfg);
+  const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+  // Split K only where the CUs would idle and K is deep: every split adds
+  // an fp32 write and read of the whole output, so it pays only when the
+  // split's own K range is long against the output tile.
   int split = 1;
-  while (tiles * split * 2 <= 256 && ksteps / (split * 2) >= 4) split *= 2;
-  pl.split = split;
+  while (tiles * split * 2 <= 256 && ksteps / (split * 2) >= 32) split *= 2;
   pl.k_per_split = ((ksteps + split - 1) / split) * KS;
   pl.split = (int)((K + pl.k_per_split - 1) / pl.k_per_split);
+  pl.x16_rows = tiles_m * BM;
+  pl.x16_pitch = ksteps * KS;
   return pl;
 }
 
+// workspace: [binary16 activations x16 | split-K partials]
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   const GemmPlan pl = plan_gemm(M, N, K, group_size);
-  return pl.split > 1 ? (size_t)pl.split * (size_t)M * (size_t)N * sizeof(float) : 0;
+  size_t b = align256((size_t)pl.x16_rows * (size_t)pl.x16_pitch * sizeof(_Float16));
+  if (pl.split > 1) b += (size_t)pl.split * (size_t)M * (size_t)N * sizeof(float);
+  return b;
 }
 
-hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, hipStream_t s) {
+hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspace,
+                       hipStream_t s) {
   GemmParams p = p0;
   const GemmPlan pl = plan_gemm(p.M, p.N, p.K, p.group_size);
   p.split = pl.split;
   p.k_per_split = pl.k_per_split;
   p.tiles_m = pl.tiles_m;
   p.tiles_n = pl.tiles_n;
+  p.x16_pitch = pl.x16_pitch;
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.x16 = reinterpret_cast<_Float16*>(ws);
+  p.partial = reinterpret_cast<float*>(
+      ws + align256((size_t)pl.x16_rows * (size_t)pl.x16_pitch * sizeof(_Float16)));
   int smode;
   if (p.group_size == 0 || p.group_size >= p.K) {
     smode = kPerChannel;
@@ -332,15 +585,43 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, hipStream_t s)
   } else {
     smode = kGeneric;
   }
+  p.log2_gs = -1;  // group index by shift when the group size is a power of two
+  if (smode != kPerChannel && (p.group_size & (p.group_size - 1)) == 0) {
+    int l2 = 0;
+    while ((1LL << l2) < p.group_size) ++l2;
+    p.log2_gs = l2;
+  }
+  // 1. activations to binary16 (RN16), permuted and zero-padded
+  const int64_t groups = pl.x16_rows * (pl.x16_pitch / 8);
+  const dim3 xgrid((unsigned)((groups + 255) / 256));
+  if (order == 0)
+    hipLaunchKernelGGL(x16_kernel<0>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
+                       pl.x16_rows, pl.x16_pitch);
+  else
+    hipLaunchKernelGGL(x16_kernel<1>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
+                       pl.x16_rows, pl.x16_pitch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 2. the GEMM
   const dim3 grid((unsigned)(pl.tiles_m * pl.tiles_n), 1, (unsigned)pl.split);
-  hipError_t e;
-  if (pl.cfg == 0) e = launch_cfg<64, 32>(p, grid, order, smode, qa4, s);
-  else e = launch_cfg<128, 64>(p, grid, order, smode, qa4, s);
+  // the branch-free kernel: power-of-two groups >= 32 or per-channel,
+  // dword-aligned rows, K a multiple of 32 (each 16-byte weight chunk lies
+  // wholly inside a row or wholly past its end: a vector load that crosses
+  // the end of its resource returns zeros for all of its bytes), and all
+  // byte offsets of its buffers below 2^32
+  const bool pow2 = smode == kGroup32 && p.log2_gs >= 5 && p.K % 32 == 0;
+  const bool small = (uint64_t)p.N * (uint64_t)p.ldq < (1ull << 32) &&
+                     (uint64_t)p.G * (uint64_t)p.lds * 4 < (1ull << 32) &&
+                     (uint64_t)pl.x16_rows * (uint64_t)pl.x16_pitch * 2 < (1ull << 32);
+  if (qa4 && small && p.K % 32 == 0 && (smode == kPerChannel || pow2))
+    e = pl.cfg == 256 ? launch_fast<256>(p, grid, order, smode == kPerChannel, s)
+                      : launch_fast<128>(p, grid, order, smode == kPerChannel, s);
+  else
+    e = pl.cfg == 256 ? launch_cfg<256>(p, grid, order, smode, qa4, s)
+                      : launch_cfg<128>(p, grid, order, smode, qa4, s);
   if (e != hipSuccess || pl.split == 1) return e;
-  const int64_t total = p.M * p.N;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     s, p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split);
-  return hipGetLastError();
+  // 3. split-K partial sums, in split order
+  return launch_splitk_reduce(p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split, s);
 }
 
 }  // namespace q4

@@ -284,13 +284,38 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial,
                                      const float* __restrict__ bias,
                                      float* __restrict__ out, int64_t ldo,
                                      int64_t M, int64_t N, int split) {
+  // four consecutive outputs per thread when the rows allow 16-byte access
+  const bool vec = (N % 4 == 0) && (ldo % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(out) % 16 == 0);
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (vec) {
+    const int64_t e = 4 * idx;
+    if (e >= M * N) return;
+    const int64_t m = e / N, n = e % N;
+    float4 v = *reinterpret_cast<const float4*>(partial + e);
+    for (int z = 1; z < split; ++z) {
+      const float4 w = *reinterpret_cast<const float4*>(partial + (int64_t)z * M * N + e);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    if (bias) { v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3]; }
+    *reinterpret_cast<float4*>(out + m * ldo + n) = v;
+    return;
+  }
   if (idx >= M * N) return;
   const int64_t m = idx / N, n = idx % N;
   float v = partial[idx];
   for (int z = 1; z < split; ++z) v += partial[(int64_t)z * M * N + idx];
   if (bias) v += bias[n];
   out[m * ldo + n] = v;
+}
+
+hipError_t launch_splitk_reduce(const float* partial, const float* bias, float* out, int64_t ldo,
+                                int64_t M, int64_t N, int split, hipStream_t s) {
+  const bool vec = (N % 4 == 0) && (ldo % 4 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+  const int64_t threads = vec ? (M * N) / 4 : M * N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, partial, bias, out, ldo, M, N, split);
+  return hipGetLastError();
 }
 
 // ---- host-side plan and launch ---------------------------------------------
@@ -378,10 +403,7 @@ hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s)
       : R == 4 ? launch_r<4>(p, grid, pl.waves_k, order, smode, qa4, sa16, s)
                : launch_r<2>(p, grid, pl.waves_k, order, smode, qa4, sa16, s);
   if (e != hipSuccess || pl.split == 1) return e;
-  const int64_t total = p.M * p.N;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     s, p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split);
-  return hipGetLastError();
+  return launch_splitk_reduce(p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split, s);
 }
 
 }  // namespace q4

@@ -60,6 +60,9 @@ struct GemmParams {
   float* out;
   int64_t ldo;
   float* partial;      // split-K workspace [split][M][N] (split > 1)
+  _Float16* x16;       // binary16 activations [x16_rows][x16_pitch] (workspace)
+  int64_t x16_pitch;
+  int32_t log2_gs;     // group index by shift (power-of-two group size), else -1
   int64_t M, N, K;
   int64_t k_per_split; // multiple of the K step, filled by launch_gemm
   int32_t split;
@@ -71,11 +74,13 @@ struct GemmPlan {
   int split;
   int64_t k_per_split;
   int tiles_m, tiles_n;
+  int64_t x16_rows, x16_pitch;
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
-hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, void* workspace,
+                       hipStream_t s);
 
 // stage exports
 hipError_t launch_unpack_codes(const uint8_t* qw, int64_t ldq, int64_t N,
@@ -85,6 +90,10 @@ hipError_t launch_dequant(const uint8_t* qw, int64_t ldq, const float* scales,
                           int64_t lds, int64_t group_size, int64_t N,
                           int64_t K, int order, int dtype, void* w,
                           int64_t ldw, hipStream_t s);
+
+// out[m, n] = sum over z of partial[z][m][n] (+ bias[n]), z in order
+hipError_t launch_splitk_reduce(const float* partial, const float* bias, float* out, int64_t ldo,
+                                int64_t M, int64_t N, int split, hipStream_t s);
 
 __global__ void splitk_reduce_kernel(const float* __restrict__ partial,
                                      const float* __restrict__ bias,
