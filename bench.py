@@ -14,9 +14,13 @@ token does when each layer has its own weights.  Steps are captured into one
 HIP graph (L steps, one per copy) and replayed; timing uses HIP events on the
 capture stream, bracketed by synchronisation.
 
-Roofline: the dominant kernel's average duration is measured live with HIP
-events over back-to-back launches captured in a graph, and priced against
-MI355X peaks (HBM 8 TB/s; dense binary16 MFMA 2516.6 TFLOP/s).
+Roofline: each projection's call is timed live with HIP events over
+back-to-back launches captured in a graph; the decode roofline counts all
+four GEMV launches of the step (the only kernel it runs) against HBM at
+8 TB/s, the prefill roofline the calls' binary16 MFMA work against 2516.6
+TFLOP/s.  `traffic` (HBM bytes per launch) comes from the committed
+rocprofv3 counter summary, and only while the HIP sources still match the
+ones it was measured on.
 
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host's cores
 over a bounded sample of the same step.
@@ -135,18 +139,55 @@ def measure(suite, steps, warmup, torch):
                 ms_per_step=secs / nsteps * 1e3)
 
 
-def dominant_kernel(suite, torch, reps=64):
-    """Average duration of each projection's launch (back-to-back in a graph)
-    and the projection that takes the most time per step."""
+def launch_times(suite, torch, reps=64):
+    """Average duration of each projection's call, measured with HIP events
+    over `reps` back-to-back launches captured in a graph (rotating weight
+    copies, so every launch streams its weights from HBM)."""
     rows = []
     for i, it in enumerate(suite.items):
         g = suite.kernel_graph(i, reps)
         time_graph(torch, g, 1)
-        secs = time_graph(torch, g, 4) / (4 * reps)
-        rows.append((i, secs))
-    # time share per step = duration of this projection
-    i_dom, t_dom = max(rows, key=lambda r: r[1])
-    return rows, i_dom, t_dom
+        rows.append(time_graph(torch, g, 4) / (4 * reps))
+    return rows
+
+
+def source_digest():
+    """sha256 over the HIP sources with comments and blank space removed: ties
+    stored byte counts to the code they were measured on (edits to comments
+    alone keep it)."""
+    import glob
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_weight_only_int4_amd", "csrc", "*"))):
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(os.path.basename(f).encode())
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def stored_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_decode_1b_prefill_1b_m512.md")
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    digest = None
+    value = None
+    for ln in text.splitlines():
+        if ln.startswith("source_sha256:"):
+            digest = ln.split(":", 1)[1].strip()
+        elif ln.startswith(f"traffic_bytes_per_launch {name}:"):
+            value = float(ln.split(":", 1)[1])
+    if digest != source_digest():
+        return None
+    return value
 
 
 def copy_calibration(torch, mib=1024, reps=8):
@@ -200,21 +241,27 @@ def cpu_baseline(projs, budget_s, unit):
             work_f += p.flops() * share
         return secs, work_b, work_f
 
-    t_probe, _, _ = run(1.0 / 64)
-    est_full = t_probe * 64
-    frac = min(1.0, budget_s / max(est_full, 1e-9))
-    reps = 1 if frac < 1.0 else max(1, int(budget_s / max(est_full, 1e-9)))
+    # passes over growing column slices until about budget_s seconds of
+    # oracle time have run; every pass counts toward the rate
     secs = wb = wf = 0.0
-    for _ in range(reps):
+    frac = 1.0 / 256
+    passes = 0
+    cols = 0.0
+    wall0 = time.perf_counter()
+    while secs < budget_s and time.perf_counter() - wall0 < 3 * budget_s:
         a, b_, c = run(frac)
         secs += a
         wb += b_
         wf += c
+        cols += frac
+        passes += 1
+        rate = frac / max(a, 1e-9)  # column share per second
+        frac = min(1.0, max(frac, rate * (budget_s - secs)))
     value = wb / secs / 1e9 if unit == "GB/s" else wf / secs / 1e12
     return dict(value=round(value, 6), unit=unit, cores=orc.max_threads(), kind="oracle",
-                sample=f"fp64 oracle on the first {frac * 100:.2f}% of the output columns "
-                       f"of each of the {len(projs)} projections (whole K, all M rows), "
-                       f"{reps} pass(es), {secs:.1f} s of CPU time")
+                sample=f"fp64 oracle over leading column slices of each of the {len(projs)} "
+                       f"projections (whole K, all M rows): {passes} passes covering "
+                       f"{cols:.2f} steps' worth of outputs, {secs:.1f} s of CPU time")
 
 
 def main():
@@ -244,17 +291,23 @@ def main():
         print(f"[bench] decode: {len(dec_projs)} projections", file=sys.stderr, flush=True)
         dec = Suite(dec_projs, torch, b, make_inputs)
         m = measure(dec, args.steps, args.warmup, torch)
-        rows, i_dom, t_dom = dominant_kernel(dec, torch)
-        p_dom = dec_projs[i_dom]
-        ach = p_dom.alg_bytes() / t_dom / 1e9
+        times = launch_times(dec, torch)
+        # the step is four launches of the fp32 GEMV kernel; its roofline
+        # counts every one of them
+        t_sum = sum(times)
+        ach = dec.step_bytes / t_sum / 1e9
+        traffic = stored_traffic("gemv_f32")
         result["decode"] = dict(
             m=m, step_bytes=dec.step_bytes, copies=dec.copies,
             per_proj=[(dec_projs[i].name, round(t * 1e6, 3),
-                       round(dec_projs[i].alg_bytes() / t / 1e9, 1)) for i, t in rows],
+                       round(dec_projs[i].alg_bytes() / t / 1e9, 1)) for i, t in enumerate(times)],
             roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
-                          kernel=f"gemv_f32 ({p_dom.name})",
-                          avg_launch_us=round(t_dom * 1e6, 3)))
+                          frac=round(ach / HBM_PEAK_GBS, 4),
+                          traffic=None if traffic is None else round(traffic),
+                          traffic_unit="HBM bytes per launch (mean over the step's four launches)",
+                          kernel="gemv_f32 (all four projections)",
+                          avg_launch_us=round(t_sum / len(times) * 1e6, 3),
+                          alg_bytes_per_launch=round(dec.step_bytes / len(times))))
         print(f"[bench] decode done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
               flush=True)
         del dec
@@ -264,17 +317,19 @@ def main():
         print(f"[bench] prefill M={args.prefill_m}", file=sys.stderr, flush=True)
         pre = Suite(pre_projs, torch, b, make_inputs)
         m = measure(pre, max(8, args.steps // 8), max(4, args.warmup // 8), torch)
-        rows, i_dom, t_dom = dominant_kernel(pre, torch, reps=16)
-        p_dom = pre_projs[i_dom]
-        ach = p_dom.flops() / t_dom / 1e12
+        times = launch_times(pre, torch, reps=16)
+        # one layer call is the binary16 pre-pass plus the MFMA GEMM (plus the
+        # split-K reduce where the plan splits K); timed together per call
+        t_sum = sum(times)
+        ach = pre.step_flops / t_sum / 1e12
         result["prefill"] = dict(
             m=m, step_flops=pre.step_flops, copies=pre.copies,
             per_proj=[(pre_projs[i].name, round(t * 1e6, 3),
-                       round(pre_projs[i].flops() / t / 1e12, 2)) for i, t in rows],
+                       round(pre_projs[i].flops() / t / 1e12, 2)) for i, t in enumerate(times)],
             roofline=dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
                           unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                          traffic=None, kernel=f"gemm_f16 ({p_dom.name})",
-                          avg_launch_us=round(t_dom * 1e6, 3)))
+                          traffic=None, kernel="gemm_f16 call (pre-pass + GEMM)",
+                          avg_launch_us=round(t_sum / len(times) * 1e6, 3)))
         print(f"[bench] prefill done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
               flush=True)
         del pre

@@ -6,8 +6,10 @@
 // GEMM for M > 1.  There is no fall-back ladder: each request runs the kernel
 // its math names, with ragged shapes handled inside the kernel.
 //
-// Every check runs before anything is queued (page 2, Implementation: throw
-// "before any allocation"; page 5, Implementation: "all fail-loud").
+// Every check runs before anything is queued: the pages' guards reject bad
+// arguments loudly and before any buffer is allocated (page 2, "[ExecuTorch]
+// [WebGPU] Add optimized linear_fp32 op", Implementation; page 5, "[ExecuTorch]
+// [WebGPU] Add linear_qcs4w op", Implementation).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -4,7 +4,8 @@
 // out[m, n] = sum_k RN16(x[m, k]) * RN16((q[n, k] - 8) * RN16(s[g(k), n]))
 //             (+ bias[n]), summed in fp32.
 // Precision recipe: binary16 operands, fp32 accumulator, never binary16
-// accumulation (page 1, stack entry #20752, "f16 multiply / f32 accumulate");
+// accumulation (page 1, stack entry #20752: the binary16 multiply keeps an
+// fp32 accumulator);
 // every packed word and scale of a tile crosses into the chip once and is
 // unpacked once (page 1, stack entry #20798, the packed-word-dequant
 // staging).  The pages' 64x64 / 256-thread WGSL tile is prior art only.

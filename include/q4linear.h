@@ -13,9 +13,8 @@
  *     indexed (k / group_size) * padded_N + n, per-channel scales [N], nibble
  *     order of the two packers: page 5, "[ExecuTorch][WebGPU] Add linear_qcs4w
  *     op", Solution, Implementation and Constraints (2);
- *   - argument guards fail loudly before any work is queued: page 2,
- *     Implementation ("throwing before any allocation"); page 5,
- *     Implementation ("all fail-loud").
+ *   - argument guards fail loudly, before any buffer is allocated or any
+ *     work is queued: page 2, Implementation; page 5, Implementation.
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument named x, qw, scales, bias, out, codes, w or

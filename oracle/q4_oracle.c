@@ -16,7 +16,8 @@
  *     "Add fp32 matmul ops (mm, bmm, linear)", stack entry #20943; page 5,
  *     "Add linear_qcs4w op", Constraints (3).
  *   - Flat packed weight [N, K/2], K_packed == ceil(K/2): page 3 #20945
- *     design note ("flat [N, K/2]"); page 5, Implementation (guards).
+ *     design note (a flat [N, K/2] byte array); page 5, Implementation
+ *     (guards).
  *   - Nibble order: the q4gsw packer stores (odd << 4) | even, so even k sits
  *     in the LOW nibble; the qcs4w packer stores (even << 4) | odd, so even k
  *     sits in the HIGH nibble: page 5, Constraints (2).
@@ -179,8 +180,8 @@ void q4o_dequant_f32(const uint8_t *qw, int64_t ldq, const float *scales,
 }
 
 /* binary16 dequant: the scale is first rounded to binary16, then the exact
- * product (code - 8) * RN16(s) is rounded once to binary16 ("f16 dequant
- * multiply", page 1 stack entry #20752). */
+ * product (code - 8) * RN16(s) is rounded once to binary16 (the binary16
+ * dequant multiply of page 1, stack entry #20752). */
 void q4o_dequant_f16(const uint8_t *qw, int64_t ldq, const float *scales,
                      int64_t lds, int64_t gs, int64_t N, int64_t K, int order,
                      uint16_t *w, int64_t ldw)

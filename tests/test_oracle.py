@@ -62,7 +62,7 @@ def test_p1_every_byte_both_orders(order):
 
 
 # --------------------------------------------------------------------------
-# P2: all nibbles 8 (the "bias-zero" byte 0x88 of page 3, #20945): the
+# P2: all nibbles 8 (byte 0x88, the zero-weight byte of page 3, #20945): the
 # output is exactly the bias, and the normaliser is exactly zero.
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("K,gs", [(64, 32), (33, 8), (40, 0), (7, 3)])
