@@ -16,22 +16,18 @@
 //    order described below, zero-padded to whole tiles, into the workspace;
 //    the GEMM then reads 2 bytes per activation instead of 4 on every
 //    column tile that reuses it, and needs no row or K masks for them.
-//  * A workgroup owns a 128 x 256 output tile (8 waves, 2 x 4) when such
-//    tiles alone fill the CUs, else 128 x 128 (4 waves, 2 x 2); each wave
-//    a 64 x 64 sub-tile of four 32x32 MFMA blocks.
-//  * K advances 64 per step.  Each step the workgroup stages in LDS the
-//    activation tile (128 x 64 binary16, copied) and the weight tile: 256
-//    or 128 columns x 64 k of packed bytes, one 16-byte load per thread, unpacked
-//    with v_and_or_b32 / v_pk_add_f16 and scaled with v_pk_mul_f16 once per
-//    tile and shared by both wave rows.  The LDS tiles are double-buffered
-//    and the global loads run three steps ahead in a register ring, so
-//    their latency hides behind the MFMAs of the steps in between.
+//  * Workgroups own 128 x 128 output tiles; K advances 64 per step.
 //  * Inside every 8-element group the k order follows the nibble order of
 //    the packed word (pairs (i, i+4)); the activations are stored with the
 //    same permutation, so A and B fragments pair up k for k.
-//  * Interior column tiles take code without bounds checks; ragged N and K
-//    are masked in the edge code (0x88 bytes, predicated stores); no
-//    fall-back kernel.
+//  * Two kernels.  The pipelined one (aligned rows, K % 32 == 0, power-of-
+//    two groups >= 32 or per-channel scales) streams every operand into an
+//    LDS ring with buffer loads that write LDS directly, and unpacks each
+//    weight word once, in registers, into MFMA operands (details at the
+//    kernel).  The general one takes every other shape: any group size,
+//    unaligned rows, ragged K; it stages binary16 weight tiles in LDS from a
+//    register ring of global loads and masks the edges (0x88 bytes past the
+//    end of a row, predicated stores).  No fall-back kernel beyond these.
 //  * Split-K (grid.z > 1), only for deep K on few tiles, writes fp32
 //    partials to the workspace; the shared reduce kernel sums them in split
 //    order and adds the bias.
@@ -46,36 +42,37 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 constexpr int KS = 64;          // k per pipeline step
 constexpr int PITCH = KS + 8;   // LDS row pitch in halves
 constexpr int BM = 128;         // output rows per workgroup
-constexpr int DEPTH = 3;        // steps of global loads in flight
+constexpr int DEPTH = 3;        // steps of global loads in flight (general kernel)
 
 enum ScaleMode : int { kPerChannel = 0, kGroup32 = 1, kGroup8 = 2, kGeneric = 3 };
 
 // x16[r * kp + k] = RN16(x[r, k']) for r < mp, k < kp, where inside each
 // group of 8 the k' follow the nibble order of the packed words (pairs
-// (i, i + 4)); rows >= M and k >= K are zero.  One thread per 8 elements.
+// (i, i + 4)); rows >= M and k >= K are zero.  A thread converts 8
+// elements; a workgroup covers 2048 k of a row, grid.y strides the rows.
 template <int ORDER>
 __global__ void __launch_bounds__(256)
 x16_kernel(const float* __restrict__ x, int64_t ldx, int64_t M, int64_t K,
            _Float16* __restrict__ x16, int64_t mp, int64_t kp) {
-  const int64_t groups = kp / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= mp * groups) return;
-  const int64_t r = idx / groups, k0 = 8 * (idx % groups);
-  const float* src = x + r * ldx + k0;
-  float v[8];
-  if (r < M && k0 + 8 <= K) {
-    const f32x4_a4 a = *reinterpret_cast<const f32x4_a4*>(src);
-    const f32x4_a4 b = *reinterpret_cast<const f32x4_a4*>(src + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
+  const int64_t k0 = (int64_t)blockIdx.x * 2048 + 8 * threadIdx.x;
+  if (k0 >= kp) return;
+  for (int64_t r = blockIdx.y; r < mp; r += gridDim.y) {
+    const float* src = x + r * ldx + k0;
+    float v[8];
+    if (r < M && k0 + 8 <= K) {
+      const f32x4_a4 a = *reinterpret_cast<const f32x4_a4*>(src);
+      const f32x4_a4 b = *reinterpret_cast<const f32x4_a4*>(src + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (r < M && k0 + i < K) ? src[i] : 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = (r < M && k0 + i < K) ? src[i] : 0.0f;
+    }
+    h8 h;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) h[sl] = (_Float16)v[pair_k<ORDER>(sl >> 1, sl & 1)];
+    *reinterpret_cast<h8*>(x16 + r * kp + k0) = h;
   }
-  h8 h;
-#pragma unroll
-  for (int sl = 0; sl < 8; ++sl) h[sl] = (_Float16)v[pair_k<ORDER>(sl >> 1, sl & 1)];
-  *reinterpret_cast<h8*>(x16 + r * kp + k0) = h;
 }
 
 // BN = 128 or 256 output columns per workgroup; NT = 2 * BN threads: waves
@@ -321,192 +318,269 @@ gemm_f16_kernel(const GemmParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Fast path: power-of-two group sizes >= 32 or per-channel scales, K a
-// multiple of 32, dword-aligned weight rows, and every offset below 2^32
-// bytes.  The main loop has
-// no branches: each thread holds 32-bit offsets into three buffer resources
-// (binary16 activations, packed weights, scales), advanced by the step's k.
-// Reads past the end of a resource return 0, and the activations are zero
-// beyond M and K, so steps and columns past the edges add nothing; only the
-// epilogue stores are predicated.
-// ---------------------------------------------------------------------------
-
+// Raw buffer resource over [base, base + bytes): reads past the end
+// return 0.  bytes is clamped to the 32-bit record count.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-template <int BN, int ORDER, bool PERCH>
-__global__ void __launch_bounds__(2 * BN)
-gemm_fast_kernel(const GemmParams p) {
-  constexpr int NT = 2 * BN;
-  constexpr int WAVES_N = BN / 64;
-  constexpr int AU = BM * KS / 8 / NT;
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * PITCH];
+// ---------------------------------------------------------------------------
+// Pipelined fast path: power-of-two group sizes >= 32 or per-channel
+// scales, K a multiple of 32, dword-aligned weight rows, every byte offset
+// below 2^32; 128 x 128 tiles.
+// Global memory reaches LDS by buffer loads that write LDS directly, so no
+// registers hold data in flight and up to NSTAGE steps of activations,
+// packed weights and scales are in flight at once: the workgroup waits for
+// memory only when the pipeline runs dry.  Each of the 4 waves owns 32 output
+// columns and all 128 rows (four 32x32 MFMA blocks that share one weight
+// fragment), so every packed word is unpacked by exactly one lane, straight
+// from LDS into the MFMA operand registers.
+//
+// k order inside a step of 64: MFMA t (0..3) takes k-chunks t (lanes 0-31)
+// and 4 + t (lanes 32-63), chunk c = k 8c .. 8c+7 of the step.  A lane's
+// four chunks 4*lb + t are then one 16-byte piece of its column's 32 packed
+// bytes, and with 32-wide groups lane half lb lies in group 2*step + lb.
+//
+// LDS per stage: activations 128 rows x 8 chunks of 16 bytes, XOR-swizzled
+// (a_slot); packed weights [128 columns][32 bytes]; scales
+// [4 waves][2 halves][32 columns] floats.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Instruction order of one pipeline step, for the scheduler: a wave issues
+// in order, and an MFMA keeps the matrix unit busy for 32 cycles, so each
+// MFMA is followed by the next step's loads and LDS reads and by a few
+// dequant VALU ops, which issue while it runs.
+template <int K>
+__device__ __forceinline__ void interleave_slots() {
+  if constexpr (K < 16) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (K < 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
+    if constexpr (K < 9) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+    if constexpr (K >= 4) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    interleave_slots<K + 1>();
+  }
+}
+__device__ __forceinline__ void interleave_step() { interleave_slots<0>(); }
+
+// A wave-uniform pointer placed in scalar registers (a buffer resource must
+// live in SGPRs; an address computed with 64-bit vector arithmetic would
+// otherwise be re-checked lane by lane on every load).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt with vmcnt(n) and lgkmcnt(0), expcnt left free (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+constexpr int PIPE_BN = 128;
+constexpr int PIPE_NT = 256;
+
+// LDS slot (16 bytes) of activation chunk c (0..7) of tile row r.  Rows are
+// 128 bytes; the XOR with bits 1..3 of the row puts the 16 rows that one
+// 16-lane group of a ds_read_b128 touches on 16 distinct 4-bank groups.
+__device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+template <int NSTAGE>
+struct PipeSmem {
+  uint32_t a[NSTAGE][BM * KS / 2];       // binary16 activations, swizzled
+  uint32_t q[NSTAGE][PIPE_BN * KS / 8];  // packed weights, 32 bytes per column
+  float s[NSTAGE][PIPE_NT];              // scales (grouped only)
+};
+
+template <int ORDER, bool PERCH, int NSTAGE>
+__global__ void __launch_bounds__(PIPE_NT)
+gemm_pipe_kernel(const GemmParams p) {
+  static_assert(NSTAGE >= 3 && NSTAGE <= 6, "pipeline depth");
+  static_assert(6 * (NSTAGE - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) PipeSmem<NSTAGE> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wm = (tid >> 6) / WAVES_N, wn = (tid >> 6) % WAVES_N;
+  // wave index, in a scalar register: the LDS destination of a buffer load
+  // (register M0) must be the same for the whole wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, lb = lane >> 5;
   const uint32_t tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tm = (int)(tile % (uint32_t)p.tiles_m);
   const int tn = (int)(tile / (uint32_t)p.tiles_m);
   const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t n0 = (int64_t)tn * PIPE_BN;
   const int z = blockIdx.z;
   const int kz0 = (int)((int64_t)z * p.k_per_split);
   const int kz1 = (int)((kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K);
   const int nsteps = (kz1 - kz0 + KS - 1) / KS;
 
-  // buffer resources and per-thread offsets
+  // Buffer resources over the exact extents the caller guarantees; every
+  // read past them returns 0 (the range check covers the per-lane offset,
+  // which therefore carries the step's k).
   const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(p.x16 + m0 * p.x16_pitch, (uint64_t)BM * p.x16_pitch * 2);
-  uint32_t va[AU];
-#pragma unroll
-  for (int u = 0; u < AU; ++u) {
-    const int unit = tid + u * NT;
-    va[u] = (uint32_t)(((unit >> 3) * p.x16_pitch + 8 * (unit & 7)) * 2);
-  }
-  const int bcol = tid >> 1, bhalf = tid & 1;
-  const int64_t ncol = n0 + bcol;
-  // resource sizes are the exact extents the caller guarantees: the last
-  // weight row holds ceil(K/2) bytes, the last scale row N floats
+      make_rsrc(uniform_ptr(p.x16 + m0 * p.x16_pitch), (uint64_t)BM * p.x16_pitch * 2);
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(p.qw, (uint64_t)(p.N - 1) * p.ldq + (uint64_t)((p.K + 1) >> 1));
-  const uint32_t vq = (uint32_t)(ncol * p.ldq + 16 * bhalf);  // past the end when ncol >= N
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t vs = 0;
-  h2 s16c = {(_Float16)0.0f, (_Float16)0.0f};
-  if (PERCH) {
-    s16c = splat_f16(ncol < p.N ? p.scales[ncol] : 0.0f);
-  } else {
-    rs = make_rsrc(p.scales, ((uint64_t)(p.G - 1) * p.lds + (uint64_t)p.N) * 4);
-    // with 32-wide groups the two halves of a step sit in consecutive groups
-    vs = (uint32_t)((ncol + (p.log2_gs == 5 ? bhalf * p.lds : 0)) * 4);
-  }
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.scales, ((uint64_t)(p.G - 1) * p.lds + (uint64_t)p.N) * 4);
 
-  struct Stage {
-    u32x4 a[AU];
-    u32x4 q;
-    float s;
-  };
-  // The step offset goes into the per-lane offset (not the scalar one),
-  // because the hardware range check covers only the per-lane offset: every
-  // byte read is then checked against the resource size, and reads past it
-  // return 0.
-  auto load = [&](int step, Stage& st) {
+  // this lane's activation slots: wave w fills slots 256w .. 256w + 255
+  uint32_t va[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = (w * 4 + u) * 64 + lane;  // slot j = a_slot(row, c)
+    const int row = j >> 3, c = (j & 7) ^ ((row >> 1) & 7);
+    va[u] = (uint32_t)((row * p.x16_pitch + 8 * c) * 2);
+  }
+  // packed weights: lane -> column 32w + lane/2, 16-byte half lane & 1
+  const uint32_t vq = (uint32_t)((n0 + 32 * w + (lane >> 1)) * p.ldq + 16 * (lane & 1));
+  // scales: lane -> half lb's group, column 32w + li
+  const uint32_t vs = (uint32_t)((n0 + 32 * w + li) * 4);
+  const uint32_t lds4 = (uint32_t)(p.lds * 4);
+  const int l2g = p.log2_gs;
+
+  auto issue = [&](int st, int step) {
     const uint32_t kb = (uint32_t)(kz0 + step * KS);
 #pragma unroll
-    for (int u = 0; u < AU; ++u)
-      st.a[u] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, va[u] + 2 * kb, 0, 0));
-    st.q = __builtin_bit_cast(u32x4,
-                              __builtin_amdgcn_raw_buffer_load_b128(rq, vq + (kb >> 1), 0, 0));
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_ptr_t)((char*)&sm.a[st][0] + (w * 4 + u) * 1024), 16, va[u] + 2 * kb, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rq, (lds_ptr_t)((char*)&sm.q[st][0] + w * 1024), 16, vq + (kb >> 1), 0, 0, 0);
     if (!PERCH)
-      st.s = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(
-                     rs, vs + (uint32_t)((kb >> p.log2_gs) * (uint64_t)p.lds * 4), 0, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_ptr_t)((char*)&sm.s[st][0] + w * 256), 4,
+          vs + ((kb + 32 * lb) >> l2g) * lds4, 0, 0, 0);
   };
+  constexpr int PER_STAGE = PERCH ? 5 : 6;  // buffer loads per stage per lane
+
+  h2 s16c = {(_Float16)0.0f, (_Float16)0.0f};
+  if (PERCH) {
+    const int64_t col = n0 + 32 * w + li;
+    s16c = splat_f16(col < p.N ? p.scales[col] : 0.0f);
+  }
   const Magic mg = Magic::make();
-  auto store = [&](const Stage& st, _Float16* A, _Float16* B) {
+
+  f16v acc[4];
 #pragma unroll
-    for (int u = 0; u < AU; ++u) {
-      const int unit = tid + u * NT;
-      *reinterpret_cast<u32x4*>(&A[(unit >> 3) * PITCH + 8 * (unit & 7)]) = st.a[u];
-    }
-    const h2 s16 = PERCH ? s16c : splat_f16(st.s);
-    const uint32_t qw4[4] = {st.q.x, st.q.y, st.q.z, st.q.w};
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      h2 c[4];
-      unpack_word(qw4[d], mg, c);
-      h2 w[4];
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) w[pp] = dequant_pair_f16(c[pp], s16);
-      const h8 hw = {w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
-      *reinterpret_cast<h8*>(&B[bcol * PITCH + 32 * bhalf + 8 * d]) = hw;
-    }
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+
+  // A step's operands, read from LDS into registers one step ahead, and its
+  // weights dequantized one step ahead: while the MFMAs of step s run, the
+  // wave issues the LDS reads of step s + 1 and unpacks its weights.
+  struct Frag {
+    h8 a[4][4];  // [t][i]: activation rows 32i + li, chunk 4 lb + t
+    h8 b[4];     // [t]: binary16 weights of this lane's column, chunk 4 lb + t
+    u32x4 q;     // packed words of this lane's column, chunks 4 lb .. 4 lb + 3
+    float s;     // scale of this lane's half-step (grouped)
   };
-  f16v acc[2][2];
+  auto read_frag = [&](int st, Frag& f) {
+    f.q = *reinterpret_cast<const u32x4*>((const char*)&sm.q[st][0] + w * 1024 + li * 32 + lb * 16);
+    if (!PERCH) f.s = sm.s[st][w * 64 + lane];
+    const char* abase = (const char*)&sm.a[st][0];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  const int li = lane & 31, lb = lane >> 5;
-  auto compute = [&](const _Float16* A, const _Float16* B) {
+      for (int i = 0; i < 4; ++i)
+        f.a[t][i] = *reinterpret_cast<const h8*>(abase + a_slot(i * 32 + li, 4 * lb + t) * 16);
+  };
+  auto dequant = [&](Frag& f) {
+    const h2 s16 = PERCH ? s16c : splat_f16(f.s);
+    const uint32_t qw4[4] = {f.q.x, f.q.y, f.q.z, f.q.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      h8 a[2], b[2];
+      h2 c[4];
+      unpack_word(qw4[t], mg, c);
+      h2 d[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const h8*>(&A[(wm * 64 + i * 32 + li) * PITCH + 32 * lb + 8 * t]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const h8*>(&B[(wn * 64 + j * 32 + li) * PITCH + 32 * lb + 8 * t]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int pp = 0; pp < 4; ++pp) d[pp] = dequant_pair_f16(c[pp], s16);
+      f.b[t] = h8{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
     }
   };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[t][i], f.b[t], acc[i], 0, 0, 0);
+  };
 
-  // Two staged steps in registers, two LDS buffers: at step s the loads of
-  // step s+2 are issued, step s is computed from LDS, and step s+1 is
-  // written to the other LDS buffer.  Loads and stores past the last step
-  // only touch data that is never computed.
-  Stage r0, r1;
-  load(0, r0);
-  load(1, r1);
-  store(r0, As[0], Bs[0]);
-  __syncthreads();
-  int step = 0;
-  for (; step + 2 <= nsteps; step += 2) {
-    load(step + 2, r0);
-    compute(As[0], Bs[0]);
-    store(r1, As[1], Bs[1]);
-    __syncthreads();
-    load(step + 3, r1);
-    compute(As[1], Bs[1]);
-    store(r0, As[0], Bs[0]);
-    __syncthreads();
+  // Pipeline.  The prologue puts steps 0 .. NSTAGE-1 in flight (one per
+  // stage) and reads step 0 into registers.  Iteration s waits for its own
+  // loads of step s + 1 (the NSTAGE-2 younger steps may still be in flight)
+  // and for its LDS reads of step s, then meets the other waves: their loads
+  // of step s + 1 have landed and their reads of step s are done, so step
+  // s's stage is refilled with step s + NSTAGE.  It then issues the LDS reads
+  // of step s + 1 and runs the MFMAs of step s.  Loads past the last step
+  // read zeros or unused bytes, are never computed, and are drained before
+  // the epilogue.
+  constexpr int UNROLL = (NSTAGE % 2 == 0) ? NSTAGE : 2 * NSTAGE;
+  Frag fa, fb;
+  wait_vm_lgkm0<0>();
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st) issue(st, st);
+  wait_vm_lgkm0<PER_STAGE * (NSTAGE - 1)>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frag(0, fa);
+  dequant(fa);
+  for (int s0 = 0; s0 < nsteps; s0 += UNROLL) {
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      if (s0 + j < nsteps) {
+        Frag& cur = (j % 2 == 0) ? fa : fb;
+        Frag& nxt = (j % 2 == 0) ? fb : fa;
+        wait_vm_lgkm0<PER_STAGE * (NSTAGE - 2)>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(j % NSTAGE, s0 + j + NSTAGE);
+        read_frag((j + 1) % NSTAGE, nxt);
+        mma(cur);
+        dequant(nxt);
+        interleave_step();
+      }
+    }
   }
-  if (step < nsteps) compute(As[0], Bs[0]);
+  wait_vm_lgkm0<0>();
 
   // epilogue: lane l, element v of a 32x32 block holds row
   // 8*(v/4) + 4*(l/32) + v%4 and column l%32
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t col = n0 + wn * 64 + j * 32 + li;
-    if (col >= p.N) continue;
+  const int64_t col = n0 + 32 * w + li;
+  if (col < p.N) {
     const float bcolv = (p.split == 1 && p.bias) ? p.bias[col] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3);
+        const int64_t row = m0 + i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3);
         if (row >= p.M) continue;
         if (p.split > 1)
-          p.partial[((int64_t)z * p.M + row) * p.N + col] = acc[i][j][v];
+          p.partial[((int64_t)z * p.M + row) * p.N + col] = acc[i][v];
         else
-          p.out[row * p.ldo + col] = acc[i][j][v] + bcolv;
+          p.out[row * p.ldo + col] = acc[i][v] + bcolv;
       }
   }
 }
 
-template <int BN, int ORDER, bool PERCH>
-hipError_t launch_fast_t(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_fast_kernel<BN, ORDER, PERCH>), grid, dim3(2 * BN), 0, s, p);
+template <int ORDER, bool PERCH>
+hipError_t launch_pipe_t(const GemmParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_pipe_kernel<ORDER, PERCH, 5>), grid, dim3(PIPE_NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <int BN>
-hipError_t launch_fast(const GemmParams& p, dim3 grid, int order, bool perch, hipStream_t s) {
-  if (order == 0) return perch ? launch_fast_t<BN, 0, true>(p, grid, s) : launch_fast_t<BN, 0, false>(p, grid, s);
-  return perch ? launch_fast_t<BN, 1, true>(p, grid, s) : launch_fast_t<BN, 1, false>(p, grid, s);
+hipError_t launch_pipe(const GemmParams& p, dim3 grid, int order, bool perch, hipStream_t s) {
+  if (order == 0) return perch ? launch_pipe_t<0, true>(p, grid, s) : launch_pipe_t<0, false>(p, grid, s);
+  return perch ? launch_pipe_t<1, true>(p, grid, s) : launch_pipe_t<1, false>(p, grid, s);
 }
 
 template <int BN, int ORDER, int SMODE, bool QA4>
@@ -537,8 +611,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   GemmPlan pl{};
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t ksteps = (K + KS - 1) / KS;
-  // 128 x 256 tiles when they alone fill the CUs, else 128 x 128
-  pl.cfg = tiles_m * ((N + 255) / 256) >= 256 ? 256 : 128;
+  // 128 x 128 output tiles
+  pl.cfg = 128;
   pl.tiles_m = (int)tiles_m;
   pl.tiles_n = (int)((N + pl.cfg - 1) / pl.cfg);
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
@@ -593,8 +667,8 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
     p.log2_gs = l2;
   }
   // 1. activations to binary16 (RN16), permuted and zero-padded
-  const int64_t groups = pl.x16_rows * (pl.x16_pitch / 8);
-  const dim3 xgrid((unsigned)((groups + 255) / 256));
+  const dim3 xgrid((unsigned)((pl.x16_pitch + 2047) / 2048),
+                   (unsigned)(pl.x16_rows < 65535 ? pl.x16_rows : 65535));
   if (order == 0)
     hipLaunchKernelGGL(x16_kernel<0>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
                        pl.x16_rows, pl.x16_pitch);
@@ -615,11 +689,9 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
                      (uint64_t)p.G * (uint64_t)p.lds * 4 < (1ull << 32) &&
                      (uint64_t)pl.x16_rows * (uint64_t)pl.x16_pitch * 2 < (1ull << 32);
   if (qa4 && small && p.K % 32 == 0 && (smode == kPerChannel || pow2))
-    e = pl.cfg == 256 ? launch_fast<256>(p, grid, order, smode == kPerChannel, s)
-                      : launch_fast<128>(p, grid, order, smode == kPerChannel, s);
+    e = launch_pipe(p, grid, order, smode == kPerChannel, s);
   else
-    e = pl.cfg == 256 ? launch_cfg<256>(p, grid, order, smode, qa4, s)
-                      : launch_cfg<128>(p, grid, order, smode, qa4, s);
+    e = launch_cfg<128>(p, grid, order, smode, qa4, s);
   if (e != hipSuccess || pl.split == 1) return e;
   // 3. split-K partial sums, in split order
   return launch_splitk_reduce(p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split, s);
