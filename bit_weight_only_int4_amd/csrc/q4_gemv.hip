@@ -11,11 +11,14 @@
 //    consecutive k at 32*l, so one wave-wide 128-bit load reads 1 KiB of one
 //    weight row and no two lanes of a wave read the same activations.  A
 //    workgroup has one wave per span (up to 8; longer K is split over
-//    grid.z) and R rows (8, 4 or 2: the most that still give >= 2048 waves);
-//    the spans' partial sums meet in LDS.
-//  * Each lane loads its activations, then its scales, then the R weight
-//    chunks, all before any arithmetic; vector loads retire in order, so the
-//    arithmetic of row r overlaps the arrival of the later rows.
+//    grid.z) times max(1, 4 / spans) row groups of R rows (2, 4 or 8, by
+//    a measured rule in plan_gemv); the spans' partial sums meet in LDS.
+//  * The workgroup's activations are read from HBM/L2 once, by buffer loads
+//    that write LDS directly, and shared by its row groups (every wave
+//    reading the same few KiB of activations from L2 would load the same
+//    cache lines thousands of times per call).  Each lane issues its scale
+//    and weight loads before it waits for the activations, so the
+//    latencies overlap.
 //  * Grouped scales are [G, N] row-major, so one row's scales lie N apart;
 //    each lane reads the scales of its chunk's group for the R consecutive
 //    rows of the workgroup, one 16-byte load per four rows.
@@ -39,6 +42,33 @@ namespace q4 {
 namespace {
 
 enum ScaleMode : int { kPerChannel = 0, kStaged = 1, kGeneric = 2 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4
+// and lgkmcnt 11:8 left free)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// a wave-uniform pointer in scalar registers (a buffer resource lives in
+// SGPRs)
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// LDS slot (16 bytes) of floats 4v .. 4v+3 of lane l's 32-k chunk of span
+// wk: the XOR with bits 1..3 of the lane puts the 16 lanes of one
+// ds_read_b128 group on 16 distinct 4-bank groups.
+__device__ __forceinline__ int x_slot(int wk, int l, int v) {
+  return wk * 512 + l * 8 + (v ^ ((l >> 1) & 7));
+}
 
 
 template <bool QA4>
@@ -136,10 +166,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Loads are issued in the order they are consumed (activations, scales,
 // then the weight rows one by one) and vector loads retire in order, so the
 // arithmetic of row r overlaps the arrival of rows r+1 .. R-1.
-template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16, bool GUARD>
+//
+// XL: the workgroup's activations arrive in LDS (xs, laid out by x_slot) by
+// buffer loads the kernel issued before this call; the lane issues its
+// scale and weight loads first, then waits for all of them, meets the other
+// waves and reads its chunk from LDS.
+template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16, bool GUARD, bool XL>
 __device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_t n0,
                                           int64_t kspan, int64_t kz1, int lane,
-                                          float (&acc)[R]) {
+                                          const float* xs, int wk, float (&acc)[R]) {
   const int64_t row_bytes = (p.K + 1) >> 1;
   int64_t k0[CPL];
   bool kfull[CPL], kany[CPL];
@@ -153,7 +188,7 @@ __device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_
   float xr[CPL][32];
   const float* xrow = p.x + m * p.ldx;
 #pragma unroll
-  for (int t = 0; t < CPL; ++t) {
+  for (int t = 0; t < CPL && !XL; ++t) {
     if (kfull[t]) {
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
@@ -203,6 +238,23 @@ __device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_
       }
     }
   }
+  if (XL) {
+    static_assert(!XL || CPL == 1, "activations in LDS: one chunk per lane");
+    // Wait for every load in flight: the activation loads and the scale and
+    // weight loads above, issued together, so the wait is about one memory
+    // latency.  (A partial count would depend on how the compiler merges
+    // adjacent loads.)
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const f4 xv = *reinterpret_cast<const f4*>(xs + 4 * x_slot(wk, lane, v));
+      xr[0][4 * v + 0] = xv.x; xr[0][4 * v + 1] = xv.y;
+      xr[0][4 * v + 2] = xv.z; xr[0][4 * v + 3] = xv.w;
+    }
+  }
   const Magic mg = Magic::make();
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -224,45 +276,66 @@ __device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_
   }
 }
 
-// Workgroup: WK waves, one per 2048*CPL span of K, over the same R rows.
-template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16>
+// Workgroup: WK waves along K (one per 2048*CPL span) times WR row groups of
+// R rows (p.waves_k, p.waves_r; WK * WR <= 8).  XL: the workgroup's
+// activations for its K range are brought into LDS once (dynamic LDS,
+// WK x 8 KiB) and shared by its WR row groups.
+template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16, bool XL>
 __global__ void __launch_bounds__(512)
 gemv_f32_kernel(const GemvParams p) {
-  __shared__ float red[8][R];
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  __shared__ float red[8 * 8 * 8];
   constexpr int SPAN = 64 * CPL * 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = p.waves_k, WR = p.waves_r, W = WK * WR;
+  const int wk = wave % WK, wr = wave / WK;
   const int64_t m = blockIdx.y;
   const int z = blockIdx.z;
-  const int64_t n0 = (int64_t)xcd_swizzle(blockIdx.x, gridDim.x) * R;
+  const int64_t n0 = ((int64_t)xcd_swizzle(blockIdx.x, gridDim.x) * WR + wr) * R;
   const int64_t kz0 = (int64_t)z * p.k_per_split;
   const int64_t kz1 = (kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K;
-  const int64_t kspan = kz0 + (int64_t)wave * SPAN;
+  const int64_t kspan = kz0 + (int64_t)wk * SPAN;
+
+  if (XL) {
+    // activations [kz0, kz1) of row m: WK * 8 wave loads of 1 KiB, spread
+    // over the W waves; reads past kz1 return zeros
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(uniform_ptr(p.x + m * p.ldx + kz0)), (short)0,
+        (int)((kz1 - kz0) * 4), 0x00020000);
+    for (int i = wave; i < WK * 8; i += W) {
+      const int j = i * 64 + lane;
+      const int span = j >> 9, l = (j >> 3) & 63, v = (j & 7) ^ ((l >> 1) & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_ptr_t)((char*)xs + i * 1024), 16,
+          (uint32_t)((span * 2048 + 32 * l + 4 * v) * 4), 0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  }
 
   float acc[R];
   if (n0 + R <= p.N && kspan + SPAN <= kz1)
-    gemv_tile<CPL, R, ORDER, SMODE, QA4, SA16, false>(p, m, n0, kspan, kz1, lane, acc);
+    gemv_tile<CPL, R, ORDER, SMODE, QA4, SA16, false, XL>(p, m, n0, kspan, kz1, lane, xs, wk, acc);
   else
-    gemv_tile<CPL, R, ORDER, SMODE, QA4, SA16, true>(p, m, n0, kspan, kz1, lane, acc);
+    gemv_tile<CPL, R, ORDER, SMODE, QA4, SA16, true, XL>(p, m, n0, kspan, kz1, lane, xs, wk, acc);
 
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
-  if (nwaves > 1) {
+  if (WK > 1) {
     if (lane == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) red[wave][r] = acc[r];
+      for (int r = 0; r < R; ++r) red[(wr * 8 + wk) * 8 + r] = acc[r];
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wk != 0) return;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float v = red[0][r];
-      for (int w = 1; w < nwaves; ++w) v += red[w][r];
+      float v = red[(wr * 8 + 0) * 8 + r];
+      for (int w = 1; w < WK; ++w) v += red[(wr * 8 + w) * 8 + r];
       acc[r] = v;
     }
   }
-  // lane r of wave 0 stores row n0 + r
+  // lane r of the row group's first wave stores row n0 + r
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t n = n0 + r;
@@ -330,17 +403,22 @@ int scale_mode(int64_t gs, int64_t K) {
 }
 
 template <int R, int ORDER, int SMODE, bool QA4, bool SA16>
-hipError_t launch_t(const GemvParams& p, dim3 grid, int nwaves, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_f32_kernel<1, R, ORDER, SMODE, QA4, SA16>), grid, dim3(64 * nwaves),
-                     0, s, p);
+hipError_t launch_t(const GemvParams& p, dim3 grid, bool xl, hipStream_t s) {
+  const int nwaves = p.waves_k * p.waves_r;
+  if (xl)
+    hipLaunchKernelGGL((gemv_f32_kernel<1, R, ORDER, SMODE, QA4, SA16, true>), grid,
+                       dim3(64 * nwaves), (size_t)p.waves_k * 8192, s, p);
+  else
+    hipLaunchKernelGGL((gemv_f32_kernel<1, R, ORDER, SMODE, QA4, SA16, false>), grid,
+                       dim3(64 * nwaves), 0, s, p);
   return hipGetLastError();
 }
 
 template <int R>
-hipError_t launch_r(const GemvParams& p, dim3 grid, int nwaves, int order, int smode, bool qa4,
+hipError_t launch_r(const GemvParams& p, dim3 grid, bool xl, int order, int smode, bool qa4,
                     bool sa16, hipStream_t s) {
 #define Q4_GEMV_CASE(O, S, A, B) \
-  if (order == O && smode == S && qa4 == A && sa16 == B) return launch_t<R, O, S, A, B>(p, grid, nwaves, s);
+  if (order == O && smode == S && qa4 == A && sa16 == B) return launch_t<R, O, S, A, B>(p, grid, xl, s);
   Q4_GEMV_CASE(0, 0, true, false) Q4_GEMV_CASE(0, 2, true, false)
   Q4_GEMV_CASE(1, 0, true, false) Q4_GEMV_CASE(1, 2, true, false)
   Q4_GEMV_CASE(0, 0, false, false) Q4_GEMV_CASE(0, 2, false, false)
@@ -362,14 +440,22 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   const int64_t spans = (K + 2047) / 2048;
   pl.split = (int)((spans + 7) / 8);  // at most 8 span-waves per workgroup
   pl.waves_k = (int)((spans + pl.split - 1) / pl.split);
-  pl.waves_r = 1;
   pl.k_per_split = (int64_t)pl.waves_k * 2048;
-  // rows per workgroup: 8 where that still gives >= 2048 waves, else 4, 2
-  int rows = 8;
-  while (rows > 2 && ((N + rows - 1) / rows) * pl.waves_k * pl.split * M < 2048) rows /= 2;
+  // Rows per wave and row groups per workgroup, from a sweep on MI355X over
+  // the Llama-shaped projections: about four waves per workgroup, four rows
+  // per wave unless that leaves fewer than 2048 waves (then two), eight
+  // only for deep K (more than four spans) where eight still give 2048.
+  auto waves = [&](int r) { return ((N + r - 1) / r) * pl.waves_k * pl.split * M; };
+  int rows = 4;
+  if (waves(4) < 2048) rows = 2;
+  if (pl.waves_k > 4 && waves(8) >= 2048) rows = 8;
   pl.rows_per_wave = rows;
-  pl.rows_per_block = rows;
-  pl.blocks_n = (N + rows - 1) / rows;
+  int wr = 4 / pl.waves_k;
+  if (wr < 1) wr = 1;
+  while (wr > 1 && (int64_t)(wr / 2) * rows >= N) wr /= 2;
+  pl.waves_r = wr;
+  pl.rows_per_block = rows * wr;
+  pl.blocks_n = (N + pl.rows_per_block - 1) / pl.rows_per_block;
   return pl;
 }
 
@@ -381,11 +467,15 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size)
 hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s) {
   GemvParams p = p0;
   const GemvPlan pl = plan_gemv(p.M, p.N, p.K, p.group_size);
-  p.rows_per_block = pl.rows_per_block;
   p.k_per_split = pl.k_per_split;
   p.split = pl.split;
   p.waves_k = pl.waves_k;
-  p.waves_r = 1;
+  // activations through LDS when every 16-byte piece of the row range is
+  // whole or wholly past its end (K % 4 == 0); else one row group per
+  // workgroup, each wave reading its activations itself
+  const bool xl = p.K % 4 == 0;
+  p.waves_r = xl ? pl.waves_r : 1;
+  const int64_t rpb = (int64_t)pl.rows_per_wave * p.waves_r;
   const int smode = scale_mode(p.group_size, p.K);
   if (smode == kPerChannel) p.group_size = 0;  // one group: scale row 0 per channel
   int l2 = 0;
@@ -397,11 +487,12 @@ hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s)
   // the scale matrix (each row group starts at a multiple of R >= 4)
   const bool sa16 = smode == kStaged && R >= 4 &&
                     (reinterpret_cast<uintptr_t>(p.scales) % 16 == 0) && (p.lds % 4 == 0);
-  const dim3 grid((unsigned)pl.blocks_n, (unsigned)p.M, (unsigned)pl.split);
+  p.rows_per_block = (int32_t)rpb;
+  const dim3 grid((unsigned)((p.N + rpb - 1) / rpb), (unsigned)p.M, (unsigned)pl.split);
   const hipError_t e =
-      R == 8   ? launch_r<8>(p, grid, pl.waves_k, order, smode, qa4, sa16, s)
-      : R == 4 ? launch_r<4>(p, grid, pl.waves_k, order, smode, qa4, sa16, s)
-               : launch_r<2>(p, grid, pl.waves_k, order, smode, qa4, sa16, s);
+      R == 8   ? launch_r<8>(p, grid, xl, order, smode, qa4, sa16, s)
+      : R == 4 ? launch_r<4>(p, grid, xl, order, smode, qa4, sa16, s)
+               : launch_r<2>(p, grid, xl, order, smode, qa4, sa16, s);
   if (e != hipSuccess || pl.split == 1) return e;
   return launch_splitk_reduce(p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split, s);
 }
