@@ -23,6 +23,12 @@
  *     sits in the HIGH nibble: page 5, Constraints (2).
  *   - Grouped scale index (k / group_size) * padded_N + n, per-channel scale
  *     scales[n]: page 5, Solution (Before/After vs q4gsw).
+ *   - Input gradient d_x[m, k] = sum_n d_out[m, n] * dequant(W)[n, k]
+ *     (contraction over N): page 3, stack entry #20943.
+ *   - Re-quantization code = clamp(round(latent / scale), -8, 7) + 8, a
+ *     zero scale giving code 8, packed into the flat [N, K/2] layout: page
+ *     3, stack entries #20945 and #20946 (the round is ATen's, ties to
+ *     even).
  *
  * Arithmetic: every dequantized weight (code - 8) * s is formed exactly in
  * fp64 (a 4-bit integer times a 24-bit significand fits in 53 bits); the sum
@@ -257,6 +263,114 @@ void q4o_linear_sampled(const float *x, int64_t ldx, const uint8_t *qw,
         }
         free(wrow);
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* Input gradient: page 3, stack entry #20943                          */
+/* ------------------------------------------------------------------ */
+
+/* One input-gradient element: ascending-n fp64 sum of d_out[m,n] * w[n,k]
+ * (wcol[n] = w[n,k]); den = sum_n |d_out[m,n] * w[n,k]|. */
+static void one_grad(const float *dout, int64_t lddo, const double *wcol,
+                     int64_t m, int64_t N, double *out, double *den)
+{
+    double acc = 0.0, d = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double p = (double)dout[m * lddo + n] * wcol[n];
+        acc += p;
+        d += fabs(p);
+    }
+    *out = acc;
+    *den = d;
+}
+
+/* Full input gradient: dx[m * K + k], den[m * K + k] (both [M, K], fp64). */
+void q4o_linear_backward(const float *dout, int64_t lddo, const uint8_t *qw,
+                         int64_t ldq, const float *scales, int64_t lds,
+                         int64_t gs, int64_t M, int64_t N, int64_t K,
+                         int order, double *dx, double *den)
+{
+#pragma omp parallel
+    {
+        double *wcol = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t k = 0; k < K; ++k) {
+            for (int64_t n = 0; n < N; ++n)
+                wcol[n] = weight_f64(qw, ldq, scales, lds, gs, n, k, order);
+            for (int64_t m = 0; m < M; ++m)
+                one_grad(dout, lddo, wcol, m, N, &dx[m * K + k], &den[m * K + k]);
+        }
+        free(wcol);
+    }
+}
+
+/* Sampled input gradient: out[i] = d_x at (ms[i], ks[i]). */
+void q4o_linear_backward_sampled(const float *dout, int64_t lddo,
+                                 const uint8_t *qw, int64_t ldq,
+                                 const float *scales, int64_t lds, int64_t gs,
+                                 int64_t N, int order, int64_t P,
+                                 const int64_t *ms, const int64_t *ks,
+                                 double *out, double *den)
+{
+#pragma omp parallel
+    {
+        double *wcol = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < P; ++i) {
+            for (int64_t n = 0; n < N; ++n)
+                wcol[n] = weight_f64(qw, ldq, scales, lds, gs, n, ks[i], order);
+            one_grad(dout, lddo, wcol, ms[i], N, &out[i], &den[i]);
+        }
+        free(wcol);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Re-quantization and packing: page 3, stack entries #20945, #20946   */
+/* ------------------------------------------------------------------ */
+
+/* The 4-bit code of a latent weight under scale s: the quotient is formed
+ * in fp32 (one IEEE division, as the fp32 buffers of the pages hold it),
+ * rounded to the nearest integer with ties to even (ATen's round),
+ * clamped to [-8, 7] and offset by 8.  A zero scale gives code 8 without
+ * dividing; so does a quotient that is not a number (reading: NaN carries
+ * no magnitude to keep). */
+static int requant_code(float latent, float s)
+{
+    if (s == 0.0f)
+        return 8;
+    float q = latent / s;
+    if (isnan(q))
+        return 8;
+    float r = nearbyintf(q); /* default rounding mode: nearest, ties to even */
+    if (r < -8.0f)
+        r = -8.0f;
+    if (r > 7.0f)
+        r = 7.0f;
+    return (int)r + 8;
+}
+
+/* qw[n * ldq + b] for b < ceil(K/2): the codes of k = 2b, 2b + 1 in the
+ * packer's nibble order (order 0: even k low, the q4gsw packer; order 1:
+ * even k high, the qcs4w packer; page 5, Constraints (2)).  With odd K the
+ * missing k = K code is 8 (a zero weight).  Bytes past ceil(K/2) in each
+ * row are left as they are. */
+void q4o_requant(const float *latent, int64_t ldl, const float *scales,
+                 int64_t lds, int64_t gs, int64_t N, int64_t K, int order,
+                 uint8_t *qw, int64_t ldq)
+{
+    int64_t Kp = (K + 1) / 2;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < Kp; ++b) {
+            int64_t k0 = 2 * b, k1 = 2 * b + 1;
+            int c0 = requant_code(latent[n * ldl + k0],
+                                  scale_of(scales, lds, gs, n, k0));
+            int c1 = k1 < K ? requant_code(latent[n * ldl + k1],
+                                           scale_of(scales, lds, gs, n, k1))
+                            : 8;
+            qw[n * ldq + b] = order == 0 ? (uint8_t)((c1 << 4) | c0)
+                                         : (uint8_t)((c0 << 4) | c1);
+        }
 }
 
 int q4o_max_threads(void) { return omp_get_max_threads(); }

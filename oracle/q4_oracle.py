@@ -48,6 +48,11 @@ def _load():
         lib.q4o_linear.argtypes = [P, I, P, I, P, I, I, P, I, I, I, C, P, P]
         lib.q4o_linear_sampled.argtypes = [P, I, P, I, P, I, I, P, I, C, I,
                                            P, P, P, P]
+        lib.q4o_linear_backward.argtypes = [P, I, P, I, P, I, I, I, I, I, C,
+                                            P, P]
+        lib.q4o_linear_backward_sampled.argtypes = [P, I, P, I, P, I, I, I, C,
+                                                    I, P, P, P, P]
+        lib.q4o_requant.argtypes = [P, I, P, I, I, I, I, C, P, I]
         lib.q4o_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -182,3 +187,60 @@ def linear_sampled(x, qw, scales, bias, ms, ns, *, K, group_size,
                                ms.size, _ptr(ms), _ptr(ns), _ptr(out),
                                _ptr(den))
     return out, den
+
+
+def linear_backward(dout, qw, scales, *, K, group_size, order="low_first"):
+    """fp64 input gradient and normaliser: (dx [M, K], den [M, K]).
+
+    dx[m, k] = sum_n dout[m, n] * w[n, k]; den = sum_n |dout[m, n] * w[n, k]|
+    (page 3, stack entry #20943).
+    """
+    _check_c(dout, np.float32, 2, "dout")
+    N, ldq, lds = _weights(qw, scales, group_size, K)
+    M, lddo = dout.shape
+    if lddo < N:
+        raise ValueError("dout row pitch below N")
+    dx = np.empty((M, K), dtype=np.float64)
+    den = np.empty((M, K), dtype=np.float64)
+    _load().q4o_linear_backward(_ptr(dout), lddo, _ptr(qw), ldq, _ptr(scales), lds,
+                                group_size, M, N, K, _order(order), _ptr(dx), _ptr(den))
+    return dx, den
+
+
+def linear_backward_sampled(dout, qw, scales, ms, ks, *, K, group_size,
+                            order="low_first"):
+    """fp64 input-gradient elements at (ms[i], ks[i])."""
+    _check_c(dout, np.float32, 2, "dout")
+    N, ldq, lds = _weights(qw, scales, group_size, K)
+    M, lddo = dout.shape
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ks = np.ascontiguousarray(ks, dtype=np.int64)
+    if ms.shape != ks.shape or ms.ndim != 1:
+        raise ValueError("ms and ks must be equal-length vectors")
+    if ms.size and (ms.min() < 0 or ms.max() >= M or ks.min() < 0
+                    or ks.max() >= K):
+        raise ValueError("sample coordinate out of range")
+    out = np.empty(ms.shape, dtype=np.float64)
+    den = np.empty(ms.shape, dtype=np.float64)
+    _load().q4o_linear_backward_sampled(_ptr(dout), lddo, _ptr(qw), ldq, _ptr(scales),
+                                        lds, group_size, N, _order(order), ms.size,
+                                        _ptr(ms), _ptr(ks), _ptr(out), _ptr(den))
+    return out, den
+
+
+def requant(latent, scales, *, group_size, order="low_first", ldq=None, fill=0):
+    """Packed codes uint8 [N, ldq] of fp32 latent weights [N, K]:
+    clamp(round(latent / s), -8, 7) + 8 with the quotient in fp32 and ties to
+    even, zero scale -> code 8, odd K padded with code 8 (page 3, stack
+    entries #20945, #20946).  Bytes past ceil(K/2) hold `fill`."""
+    _check_c(latent, np.float32, 2, "latent")
+    N, K = latent.shape
+    Kp = (K + 1) // 2
+    ldq = Kp if ldq is None else ldq
+    if ldq < Kp:
+        raise ValueError("ldq below ceil(K/2)")
+    qw = np.full((N, ldq), fill, dtype=np.uint8)
+    _, _, lds = _weights(qw, scales, group_size, K)
+    _load().q4o_requant(_ptr(latent), K, _ptr(scales), lds, group_size, N, K,
+                        _order(order), _ptr(qw), ldq)
+    return qw
