@@ -147,6 +147,84 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
   return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
 }
 
+size_t q4_linear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size,
+                                          int32_t math) {
+  if (M <= 0 || N <= 0 || K <= 0 || group_size < 0 || M >= kMaxDim || N >= kMaxDim ||
+      K >= kMaxDim)
+    return 0;
+  if (math != Q4_MATH_AUTO && math != Q4_MATH_F32) return 0;
+  return q4::bwd_workspace_bytes(M, N, K);
+}
+
+q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw, int64_t ldq,
+                             const float* scales, int64_t lds, int64_t group_size, float* dx,
+                             int64_t lddx, int64_t M, int64_t N, int64_t K,
+                             int32_t nibble_order, int32_t math, void* workspace,
+                             size_t workspace_bytes, void* stream, int32_t* path_out) {
+  if (path_out) *path_out = Q4_PATH_NONE;
+  if (M < 0 || N <= 0 || K <= 0 || group_size < 0) return Q4_ERR_INVALID_ARG;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return Q4_ERR_INVALID_ARG;
+  if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
+    return Q4_ERR_INVALID_ARG;
+  if (math != Q4_MATH_AUTO && math != Q4_MATH_F32 && math != Q4_MATH_F16)
+    return Q4_ERR_INVALID_ARG;
+  const int64_t Kp = (K + 1) / 2;
+  const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
+  if (lddo < N || ldq < Kp || lddx < K) return Q4_ERR_INVALID_ARG;
+  if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
+  if (math == Q4_MATH_F16) return Q4_ERR_UNSUPPORTED;
+  if (M == 0) return Q4_OK;
+  if (!dout || !qw || !scales || !dx) return Q4_ERR_INVALID_ARG;
+  if (!aligned(dout, 4) || !aligned(scales, 4) || !aligned(dx, 4)) return Q4_ERR_INVALID_ARG;
+  const Range r_dx = span(dx, M, lddx, K, 4);
+  const Range r_do = span(dout, M, lddo, N, 4);
+  const Range r_q = span(qw, N, ldq, Kp, 1);
+  const Range r_s = group_size == 0 ? span(scales, 1, N, N, 4) : span(scales, G, lds, N, 4);
+  if (overlap(r_dx, r_do) || overlap(r_dx, r_q) || overlap(r_dx, r_s)) return Q4_ERR_ALIAS;
+  const size_t need = q4::bwd_workspace_bytes(M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return Q4_ERR_WORKSPACE;
+    const Range r_w{reinterpret_cast<uintptr_t>(workspace),
+                    reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(r_w, r_dx) || overlap(r_w, r_do) || overlap(r_w, r_q) || overlap(r_w, r_s))
+      return Q4_ERR_ALIAS;
+  }
+  q4::BwdParams p{};
+  p.dout = dout; p.lddo = lddo; p.qw = qw; p.ldq = ldq;
+  p.scales = scales; p.lds = lds; p.group_size = group_size;
+  p.dx = dx; p.lddx = lddx; p.partial = reinterpret_cast<float*>(workspace);
+  p.M = M; p.N = N; p.K = K;
+  const bool qa4 = aligned(qw, 4) && (ldq % 4 == 0);
+  const hipError_t e =
+      q4::launch_bwd_f32(p, nibble_order, qa4, reinterpret_cast<hipStream_t>(stream));
+  if (path_out) *path_out = Q4_PATH_BWD_F32;
+  return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
+}
+
+q4_status q4_requant(const float* latent, int64_t ldl, const float* scales, int64_t lds,
+                     int64_t group_size, int64_t N, int64_t K, int32_t nibble_order,
+                     uint8_t* qw, int64_t ldq, void* stream) {
+  if (N < 0 || K <= 0 || group_size < 0 || N >= kMaxDim || K >= kMaxDim)
+    return Q4_ERR_INVALID_ARG;
+  if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
+    return Q4_ERR_INVALID_ARG;
+  const int64_t Kp = (K + 1) / 2;
+  const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
+  if (ldl < K || ldq < Kp) return Q4_ERR_INVALID_ARG;
+  if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
+  if (N == 0) return Q4_OK;
+  if (!latent || !scales || !qw) return Q4_ERR_INVALID_ARG;
+  if (!aligned(latent, 4) || !aligned(scales, 4)) return Q4_ERR_INVALID_ARG;
+  const Range r_q = span(qw, N, ldq, Kp, 1);
+  const Range r_s = group_size == 0 ? span(scales, 1, N, N, 4) : span(scales, G, lds, N, 4);
+  if (overlap(r_q, span(latent, N, ldl, K, 4)) || overlap(r_q, r_s)) return Q4_ERR_ALIAS;
+  const hipError_t e = q4::launch_requant(latent, ldl, scales, lds, group_size, N, K,
+                                          nibble_order, qw, ldq,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
+}
+
 q4_status q4_unpack_codes(const uint8_t* qw, int64_t ldq, int64_t N, int64_t K,
                           int32_t nibble_order, int8_t* codes, int64_t ldc, void* stream) {
   if (N < 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return Q4_ERR_INVALID_ARG;

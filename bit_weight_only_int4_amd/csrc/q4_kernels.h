@@ -91,6 +91,37 @@ hipError_t launch_dequant(const uint8_t* qw, int64_t ldq, const float* scales,
                           int64_t K, int order, int dtype, void* w,
                           int64_t ldw, hipStream_t s);
 
+// input gradient (fp32) and re-quantization
+struct BwdParams {
+  const float* dout;
+  int64_t lddo;
+  const uint8_t* qw;
+  int64_t ldq;
+  const float* scales;
+  int64_t lds;
+  int64_t group_size;  // 0 = per-channel
+  float* dx;
+  int64_t lddx;
+  float* partial;      // [blocks_n][M][K] when blocks_n > 1
+  int64_t M, N, K;
+  int64_t rows_per_wg; // filled by launch_bwd_f32
+  int64_t blocks_n;
+  int32_t log2_gs;     // power-of-two group size: log2, else -1
+};
+
+struct BwdPlan {
+  int mb;              // activation rows per workgroup pass (1, 2, 4)
+  int64_t blocks_m, blocks_k, blocks_n;
+  int64_t rows_per_wg;
+};
+
+BwdPlan plan_bwd(int64_t M, int64_t N, int64_t K);
+size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_bwd_f32(const BwdParams& p, int order, bool qa4, hipStream_t s);
+hipError_t launch_requant(const float* latent, int64_t ldl, const float* scales, int64_t lds,
+                          int64_t gs, int64_t N, int64_t K, int order, uint8_t* qw, int64_t ldq,
+                          hipStream_t s);
+
 // out[m, n] = sum over z of partial[z][m][n] (+ bias[n]), z in order
 hipError_t launch_splitk_reduce(const float* partial, const float* bias, float* out, int64_t ldo,
                                 int64_t M, int64_t N, int split, hipStream_t s);

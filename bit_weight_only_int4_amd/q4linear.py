@@ -19,11 +19,12 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "output overlaps an input",
           5: "HIP launch error"}
 ORDERS = {"low_first": 0, "high_first": 1}
 MATHS = {"auto": 0, "f32": 1, "f16": 2}
-PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16"}
+PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16", 3: "bwd_f32"}
 DTYPES = {torch.float32: 0, torch.float16: 1}
 
 # exported symbols of include/q4linear.h
-SYMBOLS = ("q4_linear", "q4_linear_workspace_bytes", "q4_unpack_codes",
+SYMBOLS = ("q4_linear", "q4_linear_workspace_bytes", "q4_linear_backward",
+           "q4_linear_backward_workspace_bytes", "q4_requant", "q4_unpack_codes",
            "q4_dequant", "q4_status_str", "q4_abi_version")
 
 _lib = None
@@ -59,6 +60,12 @@ def lib() -> ctypes.CDLL:
     L.q4_unpack_codes.restype = I32
     L.q4_dequant.argtypes = [P, I, P, I, I, I, I, I32, I32, P, I, P]
     L.q4_dequant.restype = I32
+    L.q4_linear_backward.argtypes = [P, I, P, I, P, I, I, P, I, I, I, I, I32, I32, P, SZ, P, P]
+    L.q4_linear_backward.restype = I32
+    L.q4_linear_backward_workspace_bytes.argtypes = [I, I, I, I, I32]
+    L.q4_linear_backward_workspace_bytes.restype = SZ
+    L.q4_requant.argtypes = [P, I, P, I, I, I, I, I32, P, I, P]
+    L.q4_requant.restype = I32
     L.q4_status_str.argtypes = [I32]
     L.q4_status_str.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
@@ -131,6 +138,67 @@ def linear(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
     if st != Q4_OK:
         raise Q4Error(st, "q4_linear")
     return (out, PATHS[path.value]) if return_path else out
+
+
+def _scales_pitch(scales: torch.Tensor, group_size: int, N: int) -> int:
+    if group_size == 0:
+        if scales.dim() != 1 or scales.stride(0) != 1 or not scales.is_cuda:
+            raise ValueError("per-channel scales must be a contiguous 1-D device tensor")
+        if scales.dtype != torch.float32:
+            raise ValueError("scales must be float32")
+        return N
+    return _rows(scales, "scales", torch.float32)
+
+
+def backward_workspace_bytes(M: int, N: int, K: int, group_size: int,
+                             math: str = "auto") -> int:
+    return int(lib().q4_linear_backward_workspace_bytes(M, N, K, group_size, MATHS[math]))
+
+
+def linear_backward(dout: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor, *, K: int,
+                    group_size: int, nibble_order: str = "low_first", math: str = "auto",
+                    dx: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, return_path: bool = False):
+    """dx[m, k] = sum_n dout[m, n] * (q[n, k] - 8) * s[g(k), n]: the input
+    gradient of ``linear``.  dout [M, N] float32; qw and scales as in linear."""
+    lddo = _rows(dout, "dout", torch.float32)
+    ldq = _rows(qw, "qw", torch.uint8)
+    M, N = dout.size(0), qw.size(0)
+    if dout.size(1) != N:
+        raise ValueError("dout must have one column per weight row")
+    lds = _scales_pitch(scales, group_size, N)
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=dout.device)
+    lddx = _rows(dx, "dx", torch.float32) if M > 0 else K
+    need = backward_workspace_bytes(M, N, K, group_size, math) if M > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dout.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    path = ctypes.c_int32(0)
+    st = lib().q4_linear_backward(_ptr(dout), lddo, _ptr(qw), ldq, _ptr(scales), lds,
+                                  group_size, _ptr(dx), lddx, M, N, K, ORDERS[nibble_order],
+                                  MATHS[math], _ptr(workspace), ws_bytes, _stream(),
+                                  ctypes.byref(path))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_linear_backward")
+    return (dx, PATHS[path.value]) if return_path else dx
+
+
+def requant(latent: torch.Tensor, scales: torch.Tensor, *, group_size: int,
+            nibble_order: str = "low_first", qw: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed codes [N, ceil(K/2)] uint8 of fp32 latent weights [N, K]:
+    clamp(round(latent / s), -8, 7) + 8, zero scale -> 8."""
+    ldl = _rows(latent, "latent", torch.float32)
+    N, K = latent.shape
+    lds = _scales_pitch(scales, group_size, N)
+    if qw is None:
+        qw = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=latent.device)
+    ldq = _rows(qw, "qw", torch.uint8)
+    st = lib().q4_requant(_ptr(latent), ldl, _ptr(scales), lds, group_size, N, K,
+                          ORDERS[nibble_order], _ptr(qw), ldq, _stream())
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_requant")
+    return qw
 
 
 def unpack_codes(qw: torch.Tensor, K: int, nibble_order: str = "low_first") -> torch.Tensor:

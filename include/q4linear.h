@@ -68,6 +68,7 @@ typedef int32_t q4_status;
 #define Q4_PATH_NONE 0      /* nothing queued (M == 0 or N == 0) */
 #define Q4_PATH_GEMV_F32 1  /* streaming fp32 GEMV, activation rows 1..M */
 #define Q4_PATH_GEMM_F16 2  /* MFMA f16 x f16 -> f32 GEMM */
+#define Q4_PATH_BWD_F32 3   /* fp32 input gradient (q4_linear_backward) */
 
 /* Element type of q4_dequant's output. */
 #define Q4_DTYPE_F32 0
@@ -126,13 +127,74 @@ q4_status q4_unpack_codes(const uint8_t *qw, int64_t ldq, int64_t N,
                           int64_t ldc, void *stream);
 
 /*
+ * q4_linear_backward -- the input gradient of the layer,
+ *
+ *   dx[m, k] = sum_n dout[m, n] * (q[n, k] - 8) * s[g(k), n]
+ *
+ * a contraction over N of the same packed weight the forward reads (page 3,
+ * "Add fp32 matmul ops (mm, bmm, linear)", stack entry #20943).
+ *
+ *   dout    float [M, lddo]       lddo >= N
+ *   qw, ldq, scales, lds, group_size, nibble_order: as in q4_linear
+ *   dx      float [M, lddx]       lddx >= K; must not overlap any input
+ *   math    Q4_MATH_AUTO or Q4_MATH_F32 (pure fp32: the weight is applied as
+ *           c * RN32(dout * s) when a packed word lies in one group, else
+ *           as RN32(c * s); fp32 sums); Q4_MATH_F16 is Q4_ERR_UNSUPPORTED
+ *   workspace     device scratch of q4_linear_backward_workspace_bytes(...)
+ *                 bytes (partial sums over row blocks of the weight), may be
+ *                 NULL when that is 0; contents on entry ignored, on exit
+ *                 undefined
+ *   stream, path_out: as in q4_linear (path Q4_PATH_BWD_F32)
+ *
+ * Sizes are validated as in q4_linear (K > 0).  M == 0 is a no-op; N == 0
+ * (an empty contraction) is Q4_ERR_INVALID_ARG.
+ * Precision: max |dx - exact| / sum_n |dout * w| about 1e-5 or better.
+ */
+q4_status q4_linear_backward(const float *dout, int64_t lddo, const uint8_t *qw,
+                             int64_t ldq, const float *scales, int64_t lds,
+                             int64_t group_size, float *dx, int64_t lddx,
+                             int64_t M, int64_t N, int64_t K, int32_t nibble_order,
+                             int32_t math, void *workspace, size_t workspace_bytes,
+                             void *stream, int32_t *path_out);
+
+/* Bytes of workspace q4_linear_backward needs (0 if none, or invalid sizes). */
+size_t q4_linear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                          int64_t group_size, int32_t math);
+
+/*
+ * q4_requant -- re-quantize fp32 latent weights under fixed scales and pack
+ * them into the layer's weight layout (page 3, stack entries #20945 and
+ * #20946):
+ *
+ *   code[n, k] = clamp(round(latent[n, k] / s[g(k), n]), -8, 7) + 8
+ *
+ * with the quotient one IEEE fp32 division and round to nearest, ties to
+ * even; a zero scale (or a quotient that is not a number) gives code 8.
+ *
+ *   latent  float [N, ldl]        ldl >= K
+ *   scales, lds, group_size       as in q4_linear
+ *   qw      uint8 [N, ldq]        ldq >= ceil(K / 2); bytes 0 .. ceil(K/2)-1
+ *                                 of each row are written in nibble_order
+ *                                 (odd K: the unused nibble holds code 8);
+ *                                 bytes past them are left untouched; must
+ *                                 not overlap latent or scales
+ *   stream  hipStream_t or NULL
+ *
+ * N == 0 is a valid no-op.  The codes are bit-exact: equal to the oracle's
+ * on every input.
+ */
+q4_status q4_requant(const float *latent, int64_t ldl, const float *scales,
+                     int64_t lds, int64_t group_size, int64_t N, int64_t K,
+                     int32_t nibble_order, uint8_t *qw, int64_t ldq, void *stream);
+
+/*
  * q4_dequant -- the dequantized weight matrix w [N, ldw], ldw >= K:
  *   Q4_DTYPE_F32: w = RN32((q - 8) * s)          (one rounding of the exact
  *                                                 product)
  *   Q4_DTYPE_F16: w = RN16((q - 8) * RN16(s))    (the scale rounded to
  *                 binary16, then one rounding of the exact product; this is
- *                 the operand the F16 layer feeds to MFMA; "f16 dequant
- *                 multiply", page 1, stack entry #20752)
+ *                 the operand the F16 layer feeds to MFMA: the binary16
+ *                 dequant multiply of page 1, stack entry #20752)
  * scales / lds / group_size as in q4_linear.  w is float* for F32 and a
  * binary16 (uint16_t bit pattern) array for F16.
  */

@@ -131,3 +131,46 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         b.lib()
+
+
+def test_backward_and_requant_validate():
+    """Argument checks of q4_linear_backward and q4_requant (no compute)."""
+    L = b.lib()
+    DO, DX, LAT = 0x70000000, 0x80000000, 0x90000000
+    path = ctypes.c_int32(-1)
+
+    def bwd(**kw):
+        a = dict(dout=DO, lddo=128, qw=Q, ldq=128, scales=S, lds=128, gs=32, dx=DX,
+                 lddx=256, M=2, N=128, K=256, order=0, math=0, ws=None, ws_bytes=0)
+        a.update(kw)
+        return L.q4_linear_backward(a["dout"], a["lddo"], a["qw"], a["ldq"], a["scales"],
+                                    a["lds"], a["gs"], a["dx"], a["lddx"], a["M"], a["N"],
+                                    a["K"], a["order"], a["math"], a["ws"], a["ws_bytes"],
+                                    None, ctypes.byref(path))
+    for kw in (dict(dout=None), dict(dx=None), dict(qw=None), dict(scales=None),
+               dict(M=-1), dict(N=0), dict(K=0), dict(gs=-1), dict(lddo=127),
+               dict(ldq=127), dict(lds=127), dict(lddx=255), dict(order=2), dict(math=5),
+               dict(dout=DO + 2), dict(dx=DX + 1)):
+        assert bwd(**kw) == INVALID, kw
+    assert bwd(math=2) == 4  # binary16 backward is not part of this build
+    for dx in (DO, Q + 8, S):
+        assert bwd(dx=dx) == ALIAS
+    assert bwd(M=0, dout=None, dx=None) == OK
+    # one block of weight rows needs no workspace; several do
+    assert L.q4_linear_backward_workspace_bytes(2, 128, 256, 32, 0) == 0
+    assert L.q4_linear_backward_workspace_bytes(2, 1024, 256, 32, 0) > 0
+    assert bwd(N=1024, lddo=1024, lds=1024) == WORKSPACE
+    assert L.q4_linear_backward_workspace_bytes(2, 128, 256, 32, 2) == 0
+
+    def rq(**kw):
+        a = dict(lat=LAT, ldl=256, scales=S, lds=128, gs=32, N=128, K=256, order=0, qw=Q,
+                 ldq=128)
+        a.update(kw)
+        return L.q4_requant(a["lat"], a["ldl"], a["scales"], a["lds"], a["gs"], a["N"],
+                            a["K"], a["order"], a["qw"], a["ldq"], None)
+    for kw in (dict(lat=None), dict(scales=None), dict(qw=None), dict(N=-1), dict(K=0),
+               dict(ldl=255), dict(ldq=127), dict(lds=127), dict(gs=-1), dict(order=2),
+               dict(lat=LAT + 2)):
+        assert rq(**kw) == INVALID, kw
+    assert rq(qw=LAT + 64) == ALIAS and rq(qw=S + 4) == ALIAS
+    assert rq(N=0, lat=None, qw=None, scales=None) == OK
