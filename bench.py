@@ -22,6 +22,10 @@ TFLOP/s.  `traffic` (HBM bytes per launch) comes from the committed
 rocprofv3 counter summary, and only while the HIP sources still match the
 ones it was measured on.
 
+The same run also times the input gradient (M = 1) and the re-quantization
+of the four projections' weights ("backward" and "requant" objects, GB/s of
+algorithmic bytes against HBM).
+
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host's cores
 over a bounded sample of the same step.
 """
@@ -48,7 +52,7 @@ def parse():
     ap.add_argument("--prefill-m", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "both"], default="both")
+    ap.add_argument("--only", choices=["decode", "prefill", "train", "both"], default="both")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 256 MiB device-to-device copy (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -113,6 +117,82 @@ class Suite:
             for r in range(reps):
                 self.launch(i, r % self.copies)
         return self.capture(body)
+
+
+class TrainSuite:
+    """The input gradient (M = 1) or the re-quantization of every projection
+    of a step, each with rotating copies of its large operand (packed weights
+    for the gradient, fp32 latents for re-quantization) so that each launch
+    reads it from HBM."""
+
+    def __init__(self, projs, torch, b, make_inputs, kind):
+        self.torch = torch
+        self.b = b
+        self.kind = kind
+        dev = torch.device("cuda")
+        self.items = []
+        per_step = 0
+        for p in projs:
+            if kind == "backward":
+                per_step += p.N * p.Kp + 4 * p.G * p.N
+            else:
+                per_step += 4 * p.N * p.K
+        self.copies = max(2, -(-ROTATE_BYTES // per_step))
+        self.step_bytes = 0
+        for p in projs:
+            _, qw, s, _ = make_inputs(p, 0)
+            g = torch.Generator().manual_seed(1)
+            sd = s.to(dev)
+            it = dict(p=p, s=sd)
+            if kind == "backward":
+                it["q"] = [qw.to(dev) for _ in range(self.copies)]
+                it["dout"] = torch.randn((1, p.N), generator=g).to(dev)
+                it["dx"] = torch.empty((1, p.K), device=dev)
+                need = b.backward_workspace_bytes(1, p.N, p.K, p.group_size)
+                it["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+                self.step_bytes += p.N * p.Kp + 4 * p.G * p.N + 4 * p.N + 4 * p.K
+            else:
+                w = b.dequant(qw.to(dev), sd, p.K, p.group_size, p.order, torch.float32)
+                it["lat"] = [w.clone() for _ in range(self.copies)]
+                it["qout"] = torch.empty((p.N, p.Kp), dtype=torch.uint8, device=dev)
+                self.step_bytes += 4 * p.N * p.K + 4 * p.G * p.N + p.N * p.Kp
+            self.items.append(it)
+        torch.cuda.synchronize()
+
+    def launch(self, i, c):
+        it = self.items[i]
+        p = it["p"]
+        if self.kind == "backward":
+            self.b.linear_backward(it["dout"], it["q"][c], it["s"], K=p.K,
+                                   group_size=p.group_size, nibble_order=p.order,
+                                   dx=it["dx"], workspace=it["ws"])
+        else:
+            self.b.requant(it["lat"][c], it["s"], group_size=p.group_size,
+                           nibble_order=p.order, qw=it["qout"])
+
+    capture = Suite.capture
+    step_graph = Suite.step_graph
+    kernel_graph = Suite.kernel_graph
+
+
+def train_measure(kind, projs, torch, b, make_inputs, steps, warmup):
+    suite = TrainSuite(projs, torch, b, make_inputs, kind)
+    m = measure(suite, steps, warmup, torch)
+    times = launch_times(suite, torch)
+    gbs = suite.step_bytes / (m["ms_per_step"] / 1e3) / 1e9
+    ach = suite.step_bytes / sum(times) / 1e9
+    res = dict(
+        value=round(gbs, 1), unit="GB/s", ms_per_step=round(m["ms_per_step"], 6),
+        steps=m["steps"], alg_bytes_per_step=suite.step_bytes, rotating_copies=suite.copies,
+        roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="bwd_f32 (+ row-block reduce)" if kind == "backward"
+                      else "requant",
+                      avg_launch_us=round(sum(times) / len(times) * 1e6, 3)),
+        per_projection_us=[(p.name, round(t * 1e6, 3)) for p, t in zip(projs, times)])
+    del suite
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_graph(torch, g, replays):
@@ -335,6 +415,14 @@ def main():
         del pre
         torch.cuda.empty_cache()
 
+    if args.only in ("train", "both"):
+        for kind in ("backward", "requant"):
+            print(f"[bench] {kind}", file=sys.stderr, flush=True)
+            result[kind] = train_measure(kind, dec_projs, torch, b, make_inputs,
+                                         max(16, args.steps // 4), max(4, args.warmup // 4))
+            print(f"[bench] {kind} done: {result[kind]['ms_per_step']:.4f} ms/step",
+                  file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline and "decode" in result:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -371,6 +459,11 @@ def main():
             "roofline": pf["roofline"],
             "per_projection_us_tflops": pf["per_proj"],
         }
+    for kind, what in (("backward", "input gradient dx = dout . dequant(W), M=1"),
+                       ("requant", "re-quantization of fp32 latents into packed codes")):
+        if kind in result:
+            r = result[kind]
+            line[kind] = dict(r, config={"workload": f"decode_1b projections: {what}"})
     line["cpu_baseline"] = cpu
     if "copy" in result:
         line["copy_calibration"] = result["copy"]

@@ -2,9 +2,10 @@
 // selection and launches on the caller's stream.
 //
 // Regime (page 1, stack entry #20730: M > 1 prefill GEMM; page 4: M = 1 decode
-// GEMV): Q4_MATH_AUTO runs the fp32 GEMV for M == 1 and the binary16 MFMA
-// GEMM for M > 1.  There is no fall-back ladder: each request runs the kernel
-// its math names, with ragged shapes handled inside the kernel.
+// GEMV): Q4_MATH_AUTO runs the fp32 GEMV for M == 1 and for small batches
+// (resolve_math) and the binary16 MFMA GEMM otherwise.  There is no
+// fall-back ladder: each request runs the kernel its math names, with ragged
+// shapes handled inside the kernel.
 //
 // Every check runs before anything is queued: the pages' guards reject bad
 // arguments loudly and before any buffer is allocated (page 2, "[ExecuTorch]
@@ -39,9 +40,20 @@ bool aligned(const void* p, uintptr_t a) {
 // sizes representable in the kernels' index arithmetic
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
-int32_t resolve_math(int32_t math, int64_t M) {
-  if (math == Q4_MATH_AUTO) return M == 1 ? Q4_MATH_F32 : Q4_MATH_F16;
-  return math;
+// Q4_MATH_AUTO: fp32 for M == 1 (the GEMV) and for a few activation rows
+// whose products are few (the low-batch GEMV reads the weights once for all
+// rows and, measured on MI355X, beats the MFMA GEMM there); binary16 MFMA
+// otherwise.  Sizes only, so the workspace query and the call agree.
+int32_t resolve_math(int32_t math, int64_t M, int64_t N, int64_t K, int64_t group_size) {
+  if (math != Q4_MATH_AUTO) return math;
+  if (M == 1) return Q4_MATH_F32;
+  const bool staged = group_size == 0 || group_size >= K ||
+                      ((group_size & (group_size - 1)) == 0 && group_size >= 32 &&
+                       group_size <= 2048);
+  if (staged && K % 4 == 0 && M <= q4::gemv_lowbatch_max_rows(K) &&
+      (double)M * (double)N * (double)K <= (double)(1LL << 29))
+    return Q4_MATH_F32;
+  return Q4_MATH_F16;
 }
 
 }  // namespace
@@ -67,7 +79,7 @@ size_t q4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_
   if (M <= 0 || N <= 0 || K <= 0 || group_size < 0 || M >= kMaxDim || N >= kMaxDim ||
       K >= kMaxDim)
     return 0;
-  const int32_t m = resolve_math(math, M);
+  const int32_t m = resolve_math(math, M, N, K, group_size);
   if (m == Q4_MATH_F32) return q4::gemv_workspace_bytes(M, N, K, group_size);
   if (m == Q4_MATH_F16) return q4::gemm_workspace_bytes(M, N, K, group_size);
   return 0;
@@ -104,7 +116,7 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
   if (overlap(r_out, r_x) || overlap(r_out, r_q) || overlap(r_out, r_s) ||
       overlap(r_out, r_b))
     return Q4_ERR_ALIAS;
-  const int32_t m = resolve_math(math, M);
+  const int32_t m = resolve_math(math, M, N, K, group_size);
   const size_t need = q4_linear_workspace_bytes(M, N, K, group_size, m);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;

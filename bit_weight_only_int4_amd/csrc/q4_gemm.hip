@@ -616,11 +616,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   pl.tiles_m = (int)tiles_m;
   pl.tiles_n = (int)((N + pl.cfg - 1) / pl.cfg);
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
-  // Split K only where the CUs would idle and K is deep: every split adds
-  // an fp32 write and read of the whole output, so it pays only when the
-  // split's own K range is long against the output tile.
+  // Split K where the tiles alone leave CUs idle, down to 8 steps per split:
+  // each split adds an fp32 write and read of the output, small next to the
+  // weights when the tiles are few (small M or narrow N).
   int split = 1;
-  while (tiles * split * 2 <= 256 && ksteps / (split * 2) >= 32) split *= 2;
+  while (tiles * split * 2 <= 256 && ksteps / (split * 2) >= 8) split *= 2;
   pl.k_per_split = ((ksteps + split - 1) / split) * KS;
   pl.split = (int)((K + pl.k_per_split - 1) / pl.k_per_split);
   pl.x16_rows = tiles_m * BM;

@@ -351,6 +351,159 @@ gemv_f32_kernel(const GemvParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Low batch: MB activation rows per workgroup (2 <= M, MB in {2, 4, 8}),
+// weights streamed once for all of them.  Activations reach LDS as in the
+// XL kernel (one slice per row, MB * WK * 8 KiB); each lane unpacks its R
+// weight chunks once and applies them to every row, still pure fp32.
+// Staged or per-channel scales, dword-aligned weight rows, K % 4 == 0.
+// ---------------------------------------------------------------------------
+template <int R, int ORDER, int SMODE, bool SA16, int MB>
+__global__ void __launch_bounds__(512)
+gemv_lb_kernel(const GemvParams p) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  __shared__ float red[8 * 8 * MB * R];
+  constexpr int SPAN = 2048;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = p.waves_k, WR = p.waves_r, W = WK * WR;
+  const int wk = wave % WK, wr = wave / WK;
+  const int64_t m0 = (int64_t)blockIdx.y * MB;
+  const int z = blockIdx.z;
+  const int64_t n0 = ((int64_t)xcd_swizzle(blockIdx.x, gridDim.x) * WR + wr) * R;
+  const int64_t kz0 = (int64_t)z * p.k_per_split;
+  const int64_t kz1 = (kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K;
+  const int64_t kspan = kz0 + (int64_t)wk * SPAN;
+  const int64_t k0 = kspan + 32 * lane;
+  const bool kany = k0 < kz1, kfull = k0 + 32 <= kz1;
+  const bool interior = n0 + R <= p.N && kspan + SPAN <= kz1;
+
+  // activations of rows m0 .. m0 + MB - 1 (those < M), [kz0, kz1) each
+  for (int i = wave; i < MB * WK * 8; i += W) {
+    const int m = i / (WK * 8), ii = i % (WK * 8);
+    if (m0 + m >= p.M) continue;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(uniform_ptr(p.x + (m0 + m) * p.ldx + kz0)), (short)0,
+        (int)((kz1 - kz0) * 4), 0x00020000);
+    const int j = ii * 64 + lane;
+    const int span = j >> 9, l = (j >> 3) & 63, v = (j & 7) ^ ((l >> 1) & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)((char*)xs + i * 1024), 16,
+                                             (uint32_t)((span * 2048 + 32 * l + 4 * v) * 4),
+                                             0, 0, 0);
+  }
+  asm volatile("" ::: "memory");
+
+  // scales of this chunk's group for the R rows
+  float sv[R];
+  if (SMODE == kStaged) {
+    const int64_t g = k0 >> p.log2_gs;
+    const float* srow = p.scales + (kany ? g : 0) * p.lds + n0;
+    if (SA16 && interior) {
+#pragma unroll
+      for (int r4 = 0; r4 < R; r4 += 4) {
+        const f32x4_a4 v = *reinterpret_cast<const f32x4_a4*>(srow + r4);
+        sv[r4 + 0] = v.x; sv[r4 + 1] = v.y; sv[r4 + 2] = v.z; sv[r4 + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) sv[r] = (kany && n0 + r < p.N) ? srow[r] : 0.0f;
+    }
+  }
+  // packed weights, R rows x one 32-k chunk
+  const int64_t row_bytes = (p.K + 1) >> 1;
+  uint32_t qv[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (n0 + r < p.N && kany) {
+      load_chunk<true>(p.qw + (n0 + r) * p.ldq, k0 >> 1, row_bytes, kfull, qv[r]);
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) qv[r][d] = 0x88888888u;
+    }
+  }
+  asm volatile("" ::: "memory");
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // unpack once
+  const Magic mg = Magic::make();
+  h2 c[R][4][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) unpack_word(qv[r][d], mg, c[r][d]);
+
+  float acc[MB][R];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
+    if (m0 + m >= p.M) continue;
+    float xr[32];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const f4 xv = *reinterpret_cast<const f4*>(xs + (size_t)m * WK * 2048 +
+                                                   4 * x_slot(wk, lane, v));
+      xr[4 * v + 0] = xv.x; xr[4 * v + 1] = xv.y; xr[4 * v + 2] = xv.z; xr[4 * v + 3] = xv.w;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float part[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float a = 0.0f;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          a = __builtin_fmaf((float)c[r][d][pp].x, xr[8 * d + pair_k<ORDER>(pp, 0)], a);
+          a = __builtin_fmaf((float)c[r][d][pp].y, xr[8 * d + pair_k<ORDER>(pp, 1)], a);
+        }
+        part[d] = a;
+      }
+      const float dot = (part[0] + part[1]) + (part[2] + part[3]);
+      acc[m][r] = SMODE == kStaged ? sv[r] * dot : dot;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[m][r] = wave_sum(acc[m][r]);
+  if (WK > 1) {
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) red[((wr * 8 + wk) * MB + m) * R + r] = acc[m][r];
+    }
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float v = red[((wr * 8 + 0) * MB + m) * R + r];
+        for (int w2 = 1; w2 < WK; ++w2) v += red[((wr * 8 + w2) * MB + m) * R + r];
+        acc[m][r] = v;
+      }
+  }
+  // lane m * R + r stores (m0 + m, n0 + r)
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t mm = m0 + m, n = n0 + r;
+      if (lane != m * R + r || mm >= p.M || n >= p.N) continue;
+      float v = acc[m][r];
+      if (SMODE == kPerChannel) v *= p.scales[n];
+      if (p.split > 1) {
+        p.partial[((int64_t)z * p.M + mm) * p.N + n] = v;
+      } else {
+        if (p.bias) v += p.bias[n];
+        p.out[mm * p.ldo + n] = v;
+      }
+    }
+}
+
 }  // namespace
 
 __global__ void splitk_reduce_kernel(const float* __restrict__ partial,
@@ -414,6 +567,33 @@ hipError_t launch_t(const GemvParams& p, dim3 grid, bool xl, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int R, int ORDER, int SMODE, bool SA16, int MB>
+hipError_t launch_lb_t(const GemvParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_lb_kernel<R, ORDER, SMODE, SA16, MB>), grid,
+                     dim3(64 * p.waves_k * p.waves_r), (size_t)MB * p.waves_k * 8192, s, p);
+  return hipGetLastError();
+}
+
+template <int R, int MB>
+hipError_t launch_lb_r(const GemvParams& p, dim3 grid, int order, int smode, bool sa16,
+                       hipStream_t s) {
+#define Q4_LB_CASE(O, S, B) \
+  if (order == O && smode == S && sa16 == B) return launch_lb_t<R, O, S, B, MB>(p, grid, s);
+  Q4_LB_CASE(0, 0, false) Q4_LB_CASE(1, 0, false)
+  Q4_LB_CASE(0, 1, false) Q4_LB_CASE(1, 1, false)
+  Q4_LB_CASE(0, 1, true) Q4_LB_CASE(1, 1, true)
+#undef Q4_LB_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int MB>
+hipError_t launch_lb(const GemvParams& p, dim3 grid, int R, int order, int smode, bool sa16,
+                     hipStream_t s) {
+  return R == 8   ? launch_lb_r<8, MB>(p, grid, order, smode, sa16, s)
+         : R == 4 ? launch_lb_r<4, MB>(p, grid, order, smode, sa16, s)
+                  : launch_lb_r<2, MB>(p, grid, order, smode, sa16, s);
+}
+
 template <int R>
 hipError_t launch_r(const GemvParams& p, dim3 grid, bool xl, int order, int smode, bool qa4,
                     bool sa16, hipStream_t s) {
@@ -433,6 +613,26 @@ hipError_t launch_r(const GemvParams& p, dim3 grid, bool xl, int order, int smod
 
 }  // namespace
 
+// Activation rows per workgroup of the low-batch kernel: the next power of
+// two >= M, at most 8 and at most 8 / spans (its LDS holds MB x spans x 8 KiB
+// of activations); 1 selects the one-row kernel.
+static int lowbatch_rows(int64_t M, int waves_k) {
+  if (M < 2) return 1;
+  int cap = 8 / waves_k;
+  if (cap < 2) return 1;
+  int mb = 2;
+  while (mb < M && mb < cap) mb *= 2;
+  return mb;
+}
+
+int gemv_lowbatch_max_rows(int64_t K) {
+  const int64_t spans = (K + 2047) / 2048;
+  const int64_t split = (spans + 7) / 8;
+  const int waves_k = (int)((spans + split - 1) / split);
+  const int cap = 8 / waves_k;
+  return cap >= 2 ? cap : 1;
+}
+
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   (void)group_size;
   GemvPlan pl{};
@@ -445,7 +645,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   // the Llama-shaped projections: about four waves per workgroup, four rows
   // per wave unless that leaves fewer than 2048 waves (then two), eight
   // only for deep K (more than four spans) where eight still give 2048.
-  auto waves = [&](int r) { return ((N + r - 1) / r) * pl.waves_k * pl.split * M; };
+  pl.mb = lowbatch_rows(M, pl.waves_k);
+  const int64_t mrows = (M + pl.mb - 1) / pl.mb;  // activation row blocks
+  auto waves = [&](int r) { return ((N + r - 1) / r) * pl.waves_k * pl.split * mrows; };
   int rows = 4;
   if (waves(4) < 2048) rows = 2;
   if (pl.waves_k > 4 && waves(8) >= 2048) rows = 8;
@@ -488,11 +690,22 @@ hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s)
   const bool sa16 = smode == kStaged && R >= 4 &&
                     (reinterpret_cast<uintptr_t>(p.scales) % 16 == 0) && (p.lds % 4 == 0);
   p.rows_per_block = (int32_t)rpb;
-  const dim3 grid((unsigned)((p.N + rpb - 1) / rpb), (unsigned)p.M, (unsigned)pl.split);
-  const hipError_t e =
-      R == 8   ? launch_r<8>(p, grid, xl, order, smode, qa4, sa16, s)
-      : R == 4 ? launch_r<4>(p, grid, xl, order, smode, qa4, sa16, s)
-               : launch_r<2>(p, grid, xl, order, smode, qa4, sa16, s);
+  // several activation rows per workgroup (weights read once for all):
+  // aligned weights, activations through LDS, staged or per-channel scales
+  const int mb = (xl && qa4 && smode != kGeneric) ? pl.mb : 1;
+  hipError_t e;
+  if (mb > 1) {
+    const dim3 grid((unsigned)((p.N + rpb - 1) / rpb), (unsigned)((p.M + mb - 1) / mb),
+                    (unsigned)pl.split);
+    e = mb == 8   ? launch_lb<8>(p, grid, R, order, smode, sa16, s)
+        : mb == 4 ? launch_lb<4>(p, grid, R, order, smode, sa16, s)
+                  : launch_lb<2>(p, grid, R, order, smode, sa16, s);
+  } else {
+    const dim3 grid((unsigned)((p.N + rpb - 1) / rpb), (unsigned)p.M, (unsigned)pl.split);
+    e = R == 8   ? launch_r<8>(p, grid, xl, order, smode, qa4, sa16, s)
+        : R == 4 ? launch_r<4>(p, grid, xl, order, smode, qa4, sa16, s)
+                 : launch_r<2>(p, grid, xl, order, smode, qa4, sa16, s);
+  }
   if (e != hipSuccess || pl.split == 1) return e;
   return launch_splitk_reduce(p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split, s);
 }

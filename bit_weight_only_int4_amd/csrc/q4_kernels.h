@@ -34,6 +34,7 @@ struct GemvParams {
 
 struct GemvPlan {
   int cfg;            // chunks of 32 k per lane (1 or 2)
+  int mb;             // activation rows per workgroup (low-batch kernel), 1 = one row
   int waves_k;        // waves per workgroup along K, each over 2048 * cfg k
   int waves_r;        // waves per workgroup along N
   int rows_per_wave;  // R
@@ -44,6 +45,8 @@ struct GemvPlan {
 };
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size);
+// most activation rows one low-batch workgroup holds for this K (1: none)
+int gemv_lowbatch_max_rows(int64_t K);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
 hipError_t launch_gemv(const GemvParams& p, int order, bool qa4, hipStream_t s);
 

@@ -67,6 +67,28 @@ def test_f32_path_several_rows(M):
     check_case(x, qw, s, bias, K=2048, gs=32, order="low_first", math="f32", label="f32-M")
 
 
+# ---- low batch: several activation rows per workgroup, fp32 --------------
+@pytest.mark.parametrize("M,K,N,gs,order", [
+    (2, 2048, 515, 32, "low_first"), (3, 256, 128, 32, "high_first"),
+    (4, 8192, 700, 32, "low_first"), (5, 2008, 301, 0, "high_first"),
+    (7, 2048, 1000, 0, "high_first"), (8, 4096, 257, 128, "low_first"),
+    (9, 1024, 129, 64, "low_first"), (16, 2048, 300, 32, "high_first"),
+    (6, 6000, 90, 32, "low_first"), (2, 20000, 64, 32, "low_first"),
+])
+def test_lowbatch_f32(M, K, N, gs, order):
+    """Weights read once for all M rows; held to the fp32 bar."""
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 0), seed=M * 100 + K)
+    check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f32", label="lowbatch")
+
+
+def test_lowbatch_pitches():
+    need_gpu()
+    x, qw, s, bias = inputs(4, 2048, 200, 32, bias=True, seed=41)
+    check_case(x, qw, s, bias, K=2048, gs=32, order="low_first", math="f32",
+               pad=(3, 4, 4, 5), label="lowbatch-pitch")
+
+
 # ---- prefill GEMM (M > 1) ------------------------------------------------
 @pytest.mark.parametrize("M,K,N,gs", [
     (96, 2048, 256, 32),     # page 1: steel
@@ -80,10 +102,26 @@ def test_f32_path_several_rows(M):
 ])
 @pytest.mark.parametrize("order", ["low_first", "high_first"])
 def test_gemm_shapes(M, K, N, gs, order):
+    """The MFMA kernels at every shape (math forced to f16: for small batches
+    the automatic choice is the fp32 low-batch GEMV, tested separately)."""
     need_gpu()
     x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 0), seed=M * 7 + N,
                             x_dist=("uniform", -1, 1))
-    check_case(x, qw, s, bias, K=K, gs=gs, order=order, label="gemm")
+    check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16", label="gemm")
+
+
+@pytest.mark.parametrize("M,K,N,gs,expect", [
+    (1, 2048, 300, 32, "gemv_f32"), (4, 2048, 300, 32, "gemv_f32"),
+    (8, 2048, 8192, 32, "gemv_f32"), (2, 8192, 2048, 32, "gemv_f32"),
+    (3, 8192, 2048, 32, "gemm_f16"), (4, 2048, 128257, 0, "gemm_f16"),
+    (9, 2048, 300, 32, "gemm_f16"), (4, 2048, 300, 8, "gemm_f16"),
+])
+def test_auto_regime(M, K, N, gs, expect):
+    """The automatic choice of kernel, and its parity at that kernel's bar."""
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=M + N)
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", label="auto")
+    assert path == expect
 
 
 @pytest.mark.parametrize("math", ["f32", "f16"])
