@@ -12,7 +12,7 @@
 // is the same for every lane of a wave (a scalar load).  The 8 waves of a
 // workgroup cover consecutive row blocks of the same 512 k and add their
 // partial sums in LDS in wave order; when N spans several workgroups their
-// partial sums go to the workspace and a second kernel adds them in block
+// partial sums go to the workspace and a second kernel adds them in a fixed
 // order, so results are deterministic.
 //
 // Re-quantization (page 3, stack entries #20945 and #20946): code =
@@ -128,7 +128,47 @@ bwd_f32_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[mm][i] = 0.0f;
 
-  for (int64_t c0 = nb0; c0 < nb1; c0 += BW_CHUNK) {
+  // Interior waves (every row of the block inside N, every lane's 8 k inside
+  // K, one group per packed word): all loads of a chunk issue unconditionally,
+  // then the arithmetic runs without branches.
+  const bool fast = QA4 && nb0 + rows_w <= p.N && (int64_t)(blockIdx.x + 1) * 512 <= p.K &&
+                    (p.group_size == 0 || p.group_size % 8 == 0) && rows_w % BW_CHUNK == 0;
+  if (fast) {
+    const float* scol = p.scales + srow[0] * p.lds;
+    for (int64_t c0 = nb0; c0 < nb1; c0 += BW_CHUNK) {
+      uint32_t wv[BW_CHUNK];
+      float sv[BW_CHUNK];
+      float dv[MB][BW_CHUNK];
+#pragma unroll
+      for (int r = 0; r < BW_CHUNK; ++r) {
+        wv[r] = *reinterpret_cast<const uint32_t*>(p.qw + (c0 + r) * p.ldq + (k0 >> 1));
+        sv[r] = scol[c0 + r];
+      }
+#pragma unroll
+      for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+        for (int r = 0; r < BW_CHUNK; ++r)
+          dv[mm][r] = (m0 + mm < p.M) ? p.dout[(m0 + mm) * p.lddo + c0 + r] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < BW_CHUNK; ++r) {
+        h2 c[4];
+        unpack_word(wv[r], mg, c);
+#pragma unroll
+        for (int mm = 0; mm < MB; ++mm) {
+          const float ds = dv[mm][r] * sv[r];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            acc[mm][pair_k<ORDER>(pp, 0)] =
+                __builtin_fmaf((float)c[pp].x, ds, acc[mm][pair_k<ORDER>(pp, 0)]);
+            acc[mm][pair_k<ORDER>(pp, 1)] =
+                __builtin_fmaf((float)c[pp].y, ds, acc[mm][pair_k<ORDER>(pp, 1)]);
+          }
+        }
+      }
+    }
+  }
+
+  for (int64_t c0 = nb0; c0 < nb1 && !fast; c0 += BW_CHUNK) {
     // weight words and scales of up to BW_CHUNK rows, all in flight
     uint32_t wv[BW_CHUNK];
     float sv[BW_CHUNK];
@@ -214,16 +254,27 @@ bwd_f32_kernel(const BwdParams p) {
   }
 }
 
-// dx[m, k] = sum over row blocks b (in order) of partial[b][m][k]
+// dx[m, k] = sum over row blocks b of partial[b][m][k]: 64 elements per
+// workgroup, four threads per element; thread quarter q adds blocks q, q + 4,
+// q + 8, ... in order, and the four quarter sums are added in quarter order,
+// so the result does not depend on timing.
 __global__ void __launch_bounds__(256)
 bwd_reduce_kernel(const float* __restrict__ partial, int64_t blocks, int64_t M, int64_t K,
                   float* __restrict__ dx, int64_t lddx) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= M * K) return;
+  __shared__ float red[4][64];
+  const int t = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t e = (int64_t)blockIdx.x * 64 + t;
+  const int64_t total = M * K;
+  float v = 0.0f;
+  if (e < total) {
+#pragma unroll 4
+    for (int64_t bb = q; bb < blocks; bb += 4) v += partial[bb * total + e];
+  }
+  red[q][t] = v;
+  __syncthreads();
+  if (q != 0 || e >= total) return;
   const int64_t m = e / K, k = e % K;
-  float v = partial[e];
-  for (int64_t b = 1; b < blocks; ++b) v += partial[b * M * K + e];
-  dx[m * lddx + k] = v;
+  dx[m * lddx + k] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
 }
 
 template <int ORDER, int MB>
@@ -281,7 +332,7 @@ hipError_t launch_bwd_f32(const BwdParams& p0, int order, bool qa4, hipStream_t 
                      : launch_bwd_t<1, 1>(p, grid, qa4, s);
   if (e != hipSuccess || pl.blocks_n == 1) return e;
   const int64_t total = p.M * p.K;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, s,
                      p.partial, pl.blocks_n, p.M, p.K, p.dx, p.lddx);
   return hipGetLastError();
 }
