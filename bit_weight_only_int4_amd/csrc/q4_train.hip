@@ -53,11 +53,26 @@ requant_kernel(const float* __restrict__ latent, int64_t ldl, const float* __res
   const int64_t Kp = (K + 1) >> 1;
   if (4 * wd >= Kp) return;
   const int64_t k0 = 8 * wd;
+  // whole words with 16-byte aligned latents and one group per word: two
+  // 16-byte loads and one scale
+  const bool fast = k0 + 8 <= K && (ldl % 4) == 0 &&
+                    (reinterpret_cast<uintptr_t>(latent) % 16) == 0 && (gs == 0 || gs % 8 == 0);
   for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
     const float* lrow = latent + n * ldl;
     uint32_t c[8];
+    if (fast) {
+      const f4 a = *reinterpret_cast<const f4*>(lrow + k0);
+      const f4 b = *reinterpret_cast<const f4*>(lrow + k0 + 4);
+      int64_t srow = 0;
+      if (gs > 0) srow = log2_gs >= 0 ? (k0 >> log2_gs) : (int64_t)((uint64_t)k0 / (uint64_t)gs);
+      const float sc = scales[srow * lds + n];
+      c[0] = requant_code(a.x, sc); c[1] = requant_code(a.y, sc);
+      c[2] = requant_code(a.z, sc); c[3] = requant_code(a.w, sc);
+      c[4] = requant_code(b.x, sc); c[5] = requant_code(b.y, sc);
+      c[6] = requant_code(b.z, sc); c[7] = requant_code(b.w, sc);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 && !fast; ++i) {
       const int64_t k = k0 + i;
       if (k >= K) {
         c[i] = 8u;
