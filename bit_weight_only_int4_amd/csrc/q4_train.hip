@@ -313,6 +313,10 @@ BwdPlan plan_bwd(int64_t M, int64_t N, int64_t K) {
   // the packed weight bytes
   int64_t rows = 128;
   while (rows < 64 * M) rows *= 2;
+  // no more than N needs (rounded up to whole 16-row chunks per wave), so
+  // every wave of the workgroup has rows
+  const int64_t cap = ((N + BW_WAVES * BW_CHUNK - 1) / (BW_WAVES * BW_CHUNK)) * BW_WAVES * BW_CHUNK;
+  if (rows > cap) rows = cap < 128 ? 128 : cap;
   pl.rows_per_wg = rows;
   pl.blocks_n = (N + rows - 1) / rows;
   return pl;

@@ -158,6 +158,26 @@ def test_backward_parity(M, N, K, gs, order, pad):
     _bwd_case(M, N, K, gs, order, pad=pad, seed=M * 1000 + N + K)
 
 
+def test_backward_prefill_sized_sampled():
+    """M = 512 over a 1B-shaped weight, checked on sampled elements."""
+    need_gpu()
+    rng = np.random.default_rng(512)
+    M, N, K, gs = 512, 2048, 2048, 32
+    qw = pack(rng.integers(0, 16, (N, K)))
+    scales = _scales(rng, N, K, gs)
+    dout = rng.standard_normal((M, N)).astype(np.float32)
+    dev = torch.device("cuda")
+    got = b.linear_backward(torch.from_numpy(dout).to(dev), torch.from_numpy(qw).to(dev),
+                            torch.from_numpy(scales).to(dev), K=K, group_size=gs)
+    torch.cuda.synchronize()
+    ms = rng.integers(0, M, 400)
+    ks = rng.integers(0, K, 400)
+    ref, den = orc.linear_backward_sampled(dout, qw, scales, ms, ks, K=K, group_size=gs)
+    err = normalised_error(got.cpu().numpy()[ms, ks], ref, den)
+    log(f"[backward M=512] max normalised error={err:.3e}")
+    assert err <= 1e-5
+
+
 def test_backward_all_eights_is_exactly_zero():
     need_gpu()
     got = _bwd_case(3, 700, 1024, 32, "low_first", seed=3, all_eights=True)
