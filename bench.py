@@ -22,8 +22,9 @@ TFLOP/s.  `traffic` (HBM bytes per launch) comes from the committed
 rocprofv3 counter summary, and only while the HIP sources still match the
 ones it was measured on.
 
-The same run also times the input gradient (M = 1) and the re-quantization
-of the four projections' weights ("backward" and "requant" objects, GB/s of
+The same run also times the four projections at a small batch (M = 4, the
+kernel the automatic choice runs), the input gradient (M = 1) and the
+re-quantization of the four projections' weights ("backward" and "requant" objects, GB/s of
 algorithmic bytes against HBM).
 
 cpu_baseline: the fp64 oracle (test infrastructure) timed on this host's cores
@@ -50,6 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--prefill-m", type=int, default=512)
+    ap.add_argument("--lowbatch-m", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["decode", "prefill", "train", "both"], default="both")
@@ -393,6 +395,37 @@ def main():
         del dec
         torch.cuda.empty_cache()
 
+    if args.only in ("decode", "both") and args.lowbatch_m > 1:
+        lb_projs = [p.with_m(args.lowbatch_m) for p in dec_projs]
+        print(f"[bench] small batch M={args.lowbatch_m}", file=sys.stderr, flush=True)
+        lb = Suite(lb_projs, torch, b, make_inputs)
+        m = measure(lb, max(16, args.steps // 4), max(4, args.warmup // 4), torch)
+        times = launch_times(lb, torch)
+        paths = []
+        for it in lb.items:
+            p = it["p"]
+            _, path = b.linear(it["x"], it["qs"][0], it["ss"][0], None, K=p.K,
+                               group_size=p.group_size, nibble_order=p.order,
+                               workspace=it["ws"], return_path=True)
+            paths.append(path)
+        ach = lb.step_bytes / sum(times) / 1e9
+        result["lowbatch"] = dict(
+            value=round(lb.step_bytes / (m["ms_per_step"] / 1e3) / 1e9, 1), unit="GB/s",
+            ms_per_step=round(m["ms_per_step"], 6), steps=m["steps"],
+            alg_bytes_per_step=lb.step_bytes, rotating_weight_copies=lb.copies,
+            config={"workload": f"decode_1b projections at M={args.lowbatch_m} "
+                                "(automatic kernel choice)"},
+            roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                          kernel="per projection: " + ", ".join(paths),
+                          avg_launch_us=round(sum(times) / len(times) * 1e6, 3)),
+            per_projection_us=[(lb_projs[i].name, round(t * 1e6, 3), paths[i])
+                               for i, t in enumerate(times)])
+        print(f"[bench] small batch done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
+        del lb
+        torch.cuda.empty_cache()
+
     if args.only in ("prefill", "both"):
         print(f"[bench] prefill M={args.prefill_m}", file=sys.stderr, flush=True)
         pre = Suite(pre_projs, torch, b, make_inputs)
@@ -459,6 +492,8 @@ def main():
             "roofline": pf["roofline"],
             "per_projection_us_tflops": pf["per_proj"],
         }
+    if "lowbatch" in result:
+        line["lowbatch"] = result["lowbatch"]
     for kind, what in (("backward", "input gradient dx = dout . dequant(W), M=1"),
                        ("requant", "re-quantization of fp32 latents into packed codes")):
         if kind in result:

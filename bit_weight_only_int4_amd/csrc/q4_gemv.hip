@@ -76,7 +76,10 @@ __device__ __forceinline__ void load_chunk(const uint8_t* row, int64_t byte0,
                                            int64_t row_bytes, bool full,
                                            uint32_t (&w)[4]) {
   if (full && QA4) {
-    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(row + byte0);
+    // streamed once per call: a non-temporal load, so the weights do not
+    // displace cached lines that are reused (scales, activations); measured
+    // faster on MI355X when the weights do not fit in the caches
+    const u32x4_a4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(row + byte0));
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     return;
   }
@@ -169,7 +172,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 //
 // XL: the workgroup's activations arrive in LDS (xs, laid out by x_slot) by
 // buffer loads the kernel issued before this call; the lane issues its
-// scale and weight loads first, then waits for all of them, meets the other
+// scale and weight loads, then waits for all of them, meets the other
 // waves and reads its chunk from LDS.
 template <int CPL, int R, int ORDER, int SMODE, bool QA4, bool SA16, bool GUARD, bool XL>
 __device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_t n0,
@@ -288,8 +291,10 @@ gemv_f32_kernel(const GemvParams p) {
   constexpr int SPAN = 64 * CPL * 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // wave = wk * WR + wr; WR (row groups) is 1, 2 or 4
   const int WK = p.waves_k, WR = p.waves_r, W = WK * WR;
-  const int wk = wave % WK, wr = wave / WK;
+  const int lwr = WR == 4 ? 2 : WR == 2 ? 1 : 0;
+  const int wr = wave & (WR - 1), wk = wave >> lwr;
   const int64_t m = blockIdx.y;
   const int z = blockIdx.z;
   const int64_t n0 = ((int64_t)xcd_swizzle(blockIdx.x, gridDim.x) * WR + wr) * R;
@@ -299,7 +304,8 @@ gemv_f32_kernel(const GemvParams p) {
 
   if (XL) {
     // activations [kz0, kz1) of row m: WK * 8 wave loads of 1 KiB, spread
-    // over the W waves; reads past kz1 return zeros
+    // over the W waves; reads past kz1 return zeros.  Issued before the
+    // weight loads: measured faster here (in the low-batch kernel, after).
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(uniform_ptr(p.x + m * p.ldx + kz0)), (short)0,
         (int)((kz1 - kz0) * 4), 0x00020000);
@@ -366,8 +372,10 @@ gemv_lb_kernel(const GemvParams p) {
   constexpr int SPAN = 2048;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // wave = wk * WR + wr; WR (row groups) is 1, 2 or 4
   const int WK = p.waves_k, WR = p.waves_r, W = WK * WR;
-  const int wk = wave % WK, wr = wave / WK;
+  const int lwr = WR == 4 ? 2 : WR == 2 ? 1 : 0;
+  const int wr = wave & (WR - 1), wk = wave >> lwr;
   const int64_t m0 = (int64_t)blockIdx.y * MB;
   const int z = blockIdx.z;
   const int64_t n0 = ((int64_t)xcd_swizzle(blockIdx.x, gridDim.x) * WR + wr) * R;
@@ -377,21 +385,6 @@ gemv_lb_kernel(const GemvParams p) {
   const int64_t k0 = kspan + 32 * lane;
   const bool kany = k0 < kz1, kfull = k0 + 32 <= kz1;
   const bool interior = n0 + R <= p.N && kspan + SPAN <= kz1;
-
-  // activations of rows m0 .. m0 + MB - 1 (those < M), [kz0, kz1) each
-  for (int i = wave; i < MB * WK * 8; i += W) {
-    const int m = i / (WK * 8), ii = i % (WK * 8);
-    if (m0 + m >= p.M) continue;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(uniform_ptr(p.x + (m0 + m) * p.ldx + kz0)), (short)0,
-        (int)((kz1 - kz0) * 4), 0x00020000);
-    const int j = ii * 64 + lane;
-    const int span = j >> 9, l = (j >> 3) & 63, v = (j & 7) ^ ((l >> 1) & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)((char*)xs + i * 1024), 16,
-                                             (uint32_t)((span * 2048 + 32 * l + 4 * v) * 4),
-                                             0, 0, 0);
-  }
-  asm volatile("" ::: "memory");
 
   // scales of this chunk's group for the R rows
   float sv[R];
@@ -420,6 +413,19 @@ gemv_lb_kernel(const GemvParams p) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) qv[r][d] = 0x88888888u;
     }
+  }
+  // then the activations of rows m0 .. m0 + MB - 1 (those < M), [kz0, kz1) each
+  for (int i = wave; i < MB * WK * 8; i += W) {
+    const int m = i / (WK * 8), ii = i % (WK * 8);
+    if (m0 + m >= p.M) continue;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(uniform_ptr(p.x + (m0 + m) * p.ldx + kz0)), (short)0,
+        (int)((kz1 - kz0) * 4), 0x00020000);
+    const int j = ii * 64 + lane;
+    const int span = j >> 9, l = (j >> 3) & 63, v = (j & 7) ^ ((l >> 1) & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)((char*)xs + i * 1024), 16,
+                                             (uint32_t)((span * 2048 + 32 * l + 4 * v) * 4),
+                                             0, 0, 0);
   }
   asm volatile("" ::: "memory");
   wait_vmcnt<0>();
