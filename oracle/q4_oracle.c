@@ -25,6 +25,8 @@
  *     scales[n]: page 5, Solution (Before/After vs q4gsw).
  *   - Input gradient d_x[m, k] = sum_n d_out[m, n] * dequant(W)[n, k]
  *     (contraction over N): page 3, stack entry #20943.
+ *   - Binary16 scales (the q4f16_1 format of the page 4 decode kernels):
+ *     each scale is widened exactly to binary32, then the layer above.
  *   - Re-quantization code = clamp(round(latent / scale), -8, 7) + 8, a
  *     zero scale giving code 8, packed into the flat [N, K/2] layout: page
  *     3, stack entries #20945 and #20946 (the round is ATen's, ties to
@@ -143,6 +145,17 @@ double q4o_f16_value(uint16_t h)
     else
         v = ldexp((double)(1024 + f), E - 25);
     return sign ? -v : v;
+}
+
+/* Binary16 scales widened to binary32 (exact: every binary16 value is a
+ * binary32 value).  The layer with binary16 scales is the layer of page 3
+ * #20943 applied to these values.  (Page 4 runs its decode kernels on
+ * q4f16_1 weights, a format the pages name without defining; it is read
+ * here as 4-bit codes with binary16 group scales.) */
+void q4o_f16_values(const uint16_t *h, int64_t n, float *dst)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = (float)q4o_f16_value(h[i]);
 }
 
 void q4o_round_f16(const float *src, int64_t n, uint16_t *dst)

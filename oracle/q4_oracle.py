@@ -41,6 +41,7 @@ def _load():
         lib.q4o_f16_value.argtypes = [ctypes.c_uint16]
         lib.q4o_f16_value.restype = ctypes.c_double
         lib.q4o_round_f16.argtypes = [P, I, P]
+        lib.q4o_f16_values.argtypes = [P, I, P]
         lib.q4o_unpack_codes.argtypes = [P, I, I, I, C, P, I]
         lib.q4o_dequant_f64.argtypes = [P, I, P, I, I, I, I, C, P, I]
         lib.q4o_dequant_f32.argtypes = [P, I, P, I, I, I, I, C, P, I]
@@ -108,6 +109,21 @@ def rn_f16_bits(values) -> np.ndarray:
 
 def f16_value(bits: int) -> float:
     return float(_load().q4o_f16_value(int(bits)))
+
+
+def f16_scales_to_f32(bits) -> np.ndarray:
+    """Binary16 scales (uint16 bit patterns) as their exact float32 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    _load().q4o_f16_values(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def linear_f16_scales(x, qw, scale_bits, bias=None, *, K, group_size, order="low_first"):
+    """The layer with binary16 scales (q4f16_1 format): the scales widened
+    exactly, then linear()."""
+    return linear(x, qw, f16_scales_to_f32(scale_bits), bias, K=K, group_size=group_size,
+                  order=order)
 
 
 def unpack_codes(qw, K, order="low_first") -> np.ndarray:

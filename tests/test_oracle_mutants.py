@@ -41,6 +41,10 @@ MUTANTS = [
      "    if (s == 0.0f)\n        return 0;"),
     ("requant odd-K pad 0", "                            : 8;", "                            : 0;"),
     ("requant order swapped", "qw[n * ldq + b] = order == 0 ?", "qw[n * ldq + b] = order != 0 ?"),
+    ("binary16 scale sign dropped", "dst[i] = (float)q4o_f16_value(h[i]);",
+     "dst[i] = (float)q4o_f16_value(h[i] & 0x7FFF);"),
+    ("binary16 subnormal read as normal", "v = ldexp((double)f, -24);",
+     "v = ldexp((double)(1024 + f), -25);"),
 ]
 
 PINS = [
@@ -61,6 +65,8 @@ PINS = [
     (T2.test_requant_zero_scale_and_nan, {}),
     (T2.test_requant_packing_against_test_packer, {}),
     (T2.test_requant_golden, {}),
+    (T2.test_f16_scale_values_every_pattern, {}),
+    (T2.test_f16_scales_worked_example, {}),
 ]
 
 

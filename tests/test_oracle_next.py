@@ -12,6 +12,10 @@ clamp(round(latent / scale), -8, 7) + 8, zero scale -> code 8, packed into the
 flat [N, K/2] layout.  Pinned by the round trip through the dequant stage,
 by numpy's ties-to-even rounding on exact ties, by clamping and zero scales,
 and by the test-side packer written from the pages' packers.
+
+Binary16 scales (page 4's q4f16_1 weights, read as 4-bit codes with
+binary16 group scales): every one of the 65536 bit patterns widens to numpy's
+binary16 value, and a worked example computed by hand.
 """
 import json
 import os
@@ -184,3 +188,35 @@ def test_requant_golden():
     for order, want in g["bytes"].items():
         got = orc.requant(latent, scales, group_size=g["group_size"], order=order)
         assert got.tolist() == want, order
+
+
+# --------------------------------------------------------------------------
+# Binary16 scales
+# --------------------------------------------------------------------------
+
+def test_f16_scale_values_every_pattern():
+    """All 65536 binary16 patterns widen to the value numpy's binary16 type
+    gives them (normal, subnormal, signed zero, infinities; NaN stays NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.f16_scales_to_f32(bits)
+    want = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def test_f16_scales_worked_example():
+    """K = 4, group size 2, one row.  Codes 9, 7, 15, 0 (c = 1, -1, 7, -8),
+    x = (1, 2, 3, 4), scales 0.5 (0x3800) and 2.0 (0x4000):
+    0.5 * (1 - 2) + 2 * (21 - 32) = -22.5.  A second row with scales -2^-24
+    (0x8001, the smallest subnormal) and 65504 (0x7BFF) and all codes 15
+    (c = 7): -2^-24 * 7 * 3 + 65504 * 7 * 7 = 3209696 - 21 * 2^-24."""
+    x = np.array([[1, 2, 3, 4]], np.float32)
+    raw = np.array([[9, 7, 15, 0], [15, 15, 15, 15]])
+    bits = np.array([[0x3800, 0x8001], [0x4000, 0x7BFF]], np.uint16)
+    want = np.array([[-22.5, 3209696.0 - 21.0 * 2.0 ** -24]])
+    for order in ("low_first", "high_first"):
+        out, den = orc.linear_f16_scales(x, pack(raw, order), bits, K=4, group_size=2,
+                                         order=order)
+        assert np.array_equal(out, want), order
+        assert den[0, 0] == 0.5 * (1 + 2) + 2 * (21 + 32)
