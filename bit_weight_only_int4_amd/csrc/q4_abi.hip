@@ -85,11 +85,17 @@ size_t q4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_
   return 0;
 }
 
-q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
-                    const float* scales, int64_t lds, int64_t group_size, const float* bias,
-                    float* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
-                    int32_t nibble_order, int32_t math, void* workspace,
-                    size_t workspace_bytes, void* stream, int32_t* path_out) {
+}  // extern "C"
+
+namespace {
+
+// The layer, for fp32 scales (s32) or binary16 scales (s16); exactly one is
+// given.  Every check runs before anything is queued.
+q4_status linear_impl(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
+                      const float* s32, const _Float16* s16, int64_t lds, int64_t group_size,
+                      const float* bias, float* out, int64_t ldo, int64_t M, int64_t N,
+                      int64_t K, int32_t nibble_order, int32_t math, void* workspace,
+                      size_t workspace_bytes, void* stream, int32_t* path_out) {
   if (path_out) *path_out = Q4_PATH_NONE;
   // ---- scalar checks ----
   if (M < 0 || N < 0 || K <= 0 || group_size < 0) return Q4_ERR_INVALID_ARG;
@@ -104,14 +110,17 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
   if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return Q4_OK;
   // ---- pointer checks ----
+  const void* scales = s16 ? (const void*)s16 : (const void*)s32;
+  const int64_t selem = s16 ? 2 : 4;
   if (!x || !qw || !scales || !out) return Q4_ERR_INVALID_ARG;
-  if (!aligned(x, 4) || !aligned(scales, 4) || !aligned(out, 4) ||
+  if (!aligned(x, 4) || !aligned(scales, selem) || !aligned(out, 4) ||
       (bias && !aligned(bias, 4)))
     return Q4_ERR_INVALID_ARG;
   const Range r_out = span(out, M, ldo, N, 4);
   const Range r_x = span(x, M, ldx, K, 4);
   const Range r_q = span(qw, N, ldq, Kp, 1);
-  const Range r_s = group_size == 0 ? span(scales, 1, N, N, 4) : span(scales, G, lds, N, 4);
+  const Range r_s =
+      group_size == 0 ? span(scales, 1, N, N, selem) : span(scales, G, lds, N, selem);
   const Range r_b = span(bias, 1, N, N, 4);
   if (overlap(r_out, r_x) || overlap(r_out, r_q) || overlap(r_out, r_s) ||
       overlap(r_out, r_b))
@@ -140,7 +149,7 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
       q4::GemvParams p{};
       const int64_t mm = (M - m0 < mchunk) ? M - m0 : mchunk;
       p.x = x + m0 * ldx; p.ldx = ldx; p.qw = qw; p.ldq = ldq;
-      p.scales = scales; p.lds = lds; p.group_size = group_size; p.G = G;
+      p.scales = s32; p.scales16 = s16; p.lds = lds; p.group_size = group_size; p.G = G;
       p.bias = bias; p.out = out + m0 * ldo; p.ldo = ldo;
       p.partial = reinterpret_cast<float*>(workspace);
       p.M = mm; p.N = N; p.K = K;
@@ -150,13 +159,37 @@ q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
   } else {
     q4::GemmParams p{};
     p.x = x; p.ldx = ldx; p.qw = qw; p.ldq = ldq;
-    p.scales = scales; p.lds = lds; p.group_size = group_size; p.G = G;
+    p.scales = s32; p.scales16 = s16; p.lds = lds; p.group_size = group_size; p.G = G;
     p.bias = bias; p.out = out; p.ldo = ldo;
     p.M = M; p.N = N; p.K = K;
     e = q4::launch_gemm(p, nibble_order, qa4, workspace, s);
     if (path_out) *path_out = Q4_PATH_GEMM_F16;
   }
   return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+q4_status q4_linear(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
+                    const float* scales, int64_t lds, int64_t group_size, const float* bias,
+                    float* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                    int32_t nibble_order, int32_t math, void* workspace,
+                    size_t workspace_bytes, void* stream, int32_t* path_out) {
+  return linear_impl(x, ldx, qw, ldq, scales, nullptr, lds, group_size, bias, out, ldo, M, N,
+                     K, nibble_order, math, workspace, workspace_bytes, stream, path_out);
+}
+
+q4_status q4_linear_f16_scales(const float* x, int64_t ldx, const uint8_t* qw, int64_t ldq,
+                               const uint16_t* scales, int64_t lds, int64_t group_size,
+                               const float* bias, float* out, int64_t ldo, int64_t M,
+                               int64_t N, int64_t K, int32_t nibble_order, int32_t math,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               int32_t* path_out) {
+  return linear_impl(x, ldx, qw, ldq, nullptr, reinterpret_cast<const _Float16*>(scales), lds,
+                     group_size, bias, out, ldo, M, N, K, nibble_order, math, workspace,
+                     workspace_bytes, stream, path_out);
 }
 
 size_t q4_linear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size,

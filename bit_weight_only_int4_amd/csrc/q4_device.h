@@ -26,6 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // with one global_load_dwordx4 (dword alignment suffices for global memory).
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));  // 8-byte aligned
 
 enum Order : int { kLowFirst = 0, kHighFirst = 1 };
 
@@ -85,6 +86,13 @@ __device__ __forceinline__ h2 dequant_pair_f16(h2 c, h2 s16) { return c * s16; }
 __device__ __forceinline__ h2 splat_f16(float s) {
   const _Float16 h = (_Float16)s;  // v_cvt_f16_f32: round to nearest even
   return h2{h, h};
+}
+
+// Element i of a scale array held either as fp32 (s16 == nullptr) or as
+// binary16 (q4f16_1 weights), widened exactly.  The choice comes from a
+// kernel argument, so the branch is wave-uniform.
+__device__ __forceinline__ float scale_at(const float* s32, const _Float16* s16, int64_t i) {
+  return s16 ? (float)s16[i] : s32[i];
 }
 
 // Raw code (0..15) of nibble k of a row, one byte at a time (used by the

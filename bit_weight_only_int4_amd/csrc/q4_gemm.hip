@@ -28,6 +28,8 @@
 //    unaligned rows, ragged K; it stages binary16 weight tiles in LDS from a
 //    register ring of global loads and masks the edges (0x88 bytes past the
 //    end of a row, predicated stores).  No fall-back kernel beyond these.
+//  * Scales come as fp32 or as binary16 (q4f16_1 weights); a binary16
+//    scale is its own RN16, so both give the same operands.
 //  * Split-K (grid.z > 1), only for deep K on few tiles, writes fp32
 //    partials to the workspace; the shared reduce kernel sums them in split
 //    order and adds the bias.
@@ -102,7 +104,7 @@ struct Gemm {
   // streaming state, advanced by one step after every load
   const _Float16* pa[AU];   // the thread's activation pieces
   const uint8_t* pq;        // the thread's 16 packed bytes
-  const float* pscol;       // scales + column
+  int64_t scol;             // scale column (n, or 0 past N)
   int kc;                   // first k of the thread's chunk
   h2 s16c;                  // per-channel scale, rounded once
 
@@ -124,8 +126,13 @@ struct Gemm {
     }
     kc = kz0 + 32 * bhalf;
     pq = p.qw + (nvalid ? ncol : 0) * p.ldq + (kc >> 1);
-    pscol = p.scales + (nvalid ? ncol : 0);
-    if (SMODE == kPerChannel) s16c = splat_f16(nvalid ? *pscol : 0.0f);
+    scol = nvalid ? ncol : 0;
+    if (SMODE == kPerChannel) s16c = splat_f16(nvalid ? scale(0) : 0.0f);
+  }
+
+  // scale of this thread's column in scale row g (fp32, or binary16 widened)
+  __device__ __forceinline__ float scale(int64_t g) const {
+    return scale_at(p.scales, p.scales16, g * p.lds + scol);
   }
 
   __device__ __forceinline__ int group_of(int k) const {
@@ -158,13 +165,13 @@ struct Gemm {
         }
       }
       if (SMODE == kGroup32) {
-        st.s[0] = pscol[(int64_t)group_of(kc) * p.lds];
+        st.s[0] = scale(group_of(kc));
       } else if (SMODE == kGroup8) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           int g = group_of(kc + 8 * d);
           g = g < (int)p.G - 1 ? g : (int)p.G - 1;
-          st.s[d] = pscol[(int64_t)g * p.lds];
+          st.s[d] = scale(g);
         }
       }
     } else {
@@ -198,7 +205,7 @@ struct Gemm {
           for (int hh = 0; hh < 2; ++hh) {
             int g = (kcs + 8 * d + pair_k<ORDER>(pp, hh)) / (int)p.group_size;
             g = g < (int)p.G - 1 ? g : (int)p.G - 1;
-            const _Float16 s16 = (_Float16)(nvalid ? pscol[(int64_t)g * p.lds] : 0.0f);
+            const _Float16 s16 = (_Float16)(nvalid ? scale(g) : 0.0f);
             const _Float16 cc = hh == 0 ? c[pp].x : c[pp].y;
             if (hh == 0) w[pp].x = cc * s16; else w[pp].y = cc * s16;
           }
@@ -399,7 +406,11 @@ struct PipeSmem {
   float s[NSTAGE][PIPE_NT];              // scales (grouped only)
 };
 
-template <int ORDER, bool PERCH, int NSTAGE>
+// S16: binary16 scales (q4f16_1).  A lane's scale DMA then fetches the
+// dword that holds its column's scale and its even/odd neighbour's (N and
+// lds even, scales 4-byte aligned: no dword straddles the array's end) and
+// keeps the half of its own column parity.
+template <int ORDER, bool PERCH, int NSTAGE, bool S16>
 __global__ void __launch_bounds__(PIPE_NT)
 gemm_pipe_kernel(const GemmParams p) {
   static_assert(NSTAGE >= 3 && NSTAGE <= 6, "pipeline depth");
@@ -429,8 +440,10 @@ gemm_pipe_kernel(const GemmParams p) {
       make_rsrc(uniform_ptr(p.x16 + m0 * p.x16_pitch), (uint64_t)BM * p.x16_pitch * 2);
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(p.qw, (uint64_t)(p.N - 1) * p.ldq + (uint64_t)((p.K + 1) >> 1));
+  constexpr uint32_t SB = S16 ? 2 : 4;  // bytes per scale
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.scales, ((uint64_t)(p.G - 1) * p.lds + (uint64_t)p.N) * 4);
+      make_rsrc(S16 ? (const void*)p.scales16 : (const void*)p.scales,
+                ((uint64_t)(p.G - 1) * p.lds + (uint64_t)p.N) * SB);
 
   // this lane's activation slots: wave w fills slots 256w .. 256w + 255
   uint32_t va[4];
@@ -443,8 +456,8 @@ gemm_pipe_kernel(const GemmParams p) {
   // packed weights: lane -> column 32w + lane/2, 16-byte half lane & 1
   const uint32_t vq = (uint32_t)((n0 + 32 * w + (lane >> 1)) * p.ldq + 16 * (lane & 1));
   // scales: lane -> half lb's group, column 32w + li
-  const uint32_t vs = (uint32_t)((n0 + 32 * w + li) * 4);
-  const uint32_t lds4 = (uint32_t)(p.lds * 4);
+  const uint32_t vs = (uint32_t)(((n0 + 32 * w + li) & (S16 ? ~1 : ~0)) * SB);
+  const uint32_t lds4 = (uint32_t)(p.lds * SB);
   const int l2g = p.log2_gs;
 
   auto issue = [&](int st, int step) {
@@ -465,7 +478,7 @@ gemm_pipe_kernel(const GemmParams p) {
   h2 s16c = {(_Float16)0.0f, (_Float16)0.0f};
   if (PERCH) {
     const int64_t col = n0 + 32 * w + li;
-    s16c = splat_f16(col < p.N ? p.scales[col] : 0.0f);
+    s16c = splat_f16(col < p.N ? scale_at(p.scales, p.scales16, col) : 0.0f);
   }
   const Magic mg = Magic::make();
 
@@ -486,7 +499,11 @@ gemm_pipe_kernel(const GemmParams p) {
   };
   auto read_frag = [&](int st, Frag& f) {
     f.q = *reinterpret_cast<const u32x4*>((const char*)&sm.q[st][0] + w * 1024 + li * 32 + lb * 16);
-    if (!PERCH) f.s = sm.s[st][w * 64 + lane];
+    if (!PERCH && !S16) f.s = sm.s[st][w * 64 + lane];
+    if (!PERCH && S16) {
+      const uint32_t d = __builtin_bit_cast(uint32_t, sm.s[st][w * 64 + lane]);
+      f.s = (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> (16 * (li & 1))));
+    }
     const char* abase = (const char*)&sm.a[st][0];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -572,15 +589,21 @@ gemm_pipe_kernel(const GemmParams p) {
   }
 }
 
-template <int ORDER, bool PERCH>
+template <int ORDER, bool PERCH, bool S16>
 hipError_t launch_pipe_t(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_pipe_kernel<ORDER, PERCH, 5>), grid, dim3(PIPE_NT), 0, s, p);
+  hipLaunchKernelGGL((gemm_pipe_kernel<ORDER, PERCH, 5, S16>), grid, dim3(PIPE_NT), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_pipe(const GemmParams& p, dim3 grid, int order, bool perch, hipStream_t s) {
-  if (order == 0) return perch ? launch_pipe_t<0, true>(p, grid, s) : launch_pipe_t<0, false>(p, grid, s);
-  return perch ? launch_pipe_t<1, true>(p, grid, s) : launch_pipe_t<1, false>(p, grid, s);
+  // per-channel scales are read once per lane, outside the pipeline
+  const bool s16 = p.scales16 != nullptr && !perch;
+  if (order == 0) {
+    if (perch) return launch_pipe_t<0, true, false>(p, grid, s);
+    return s16 ? launch_pipe_t<0, false, true>(p, grid, s) : launch_pipe_t<0, false, false>(p, grid, s);
+  }
+  if (perch) return launch_pipe_t<1, true, false>(p, grid, s);
+  return s16 ? launch_pipe_t<1, false, true>(p, grid, s) : launch_pipe_t<1, false, false>(p, grid, s);
 }
 
 template <int BN, int ORDER, int SMODE, bool QA4>
@@ -688,7 +711,12 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
   const bool small = (uint64_t)p.N * (uint64_t)p.ldq < (1ull << 32) &&
                      (uint64_t)p.G * (uint64_t)p.lds * 4 < (1ull << 32) &&
                      (uint64_t)pl.x16_rows * (uint64_t)pl.x16_pitch * 2 < (1ull << 32);
-  if (qa4 && small && p.K % 32 == 0 && (smode == kPerChannel || pow2))
+  // binary16 grouped scales are fetched a dword (two columns) at a time:
+  // N and lds even and the array 4-byte aligned
+  const bool s16ok = !p.scales16 || smode == kPerChannel ||
+                     (p.N % 2 == 0 && p.lds % 2 == 0 &&
+                      reinterpret_cast<uintptr_t>(p.scales16) % 4 == 0);
+  if (qa4 && small && s16ok && p.K % 32 == 0 && (smode == kPerChannel || pow2))
     e = launch_pipe(p, grid, order, smode == kPerChannel, s);
   else
     e = launch_cfg<128>(p, grid, order, smode, qa4, s);

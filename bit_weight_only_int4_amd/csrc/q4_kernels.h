@@ -16,6 +16,7 @@ struct GemvParams {
   const uint8_t* qw;
   int64_t ldq;
   const float* scales;
+  const _Float16* scales16;  // binary16 scales instead (q4f16_1), else nullptr
   int64_t lds;
   int64_t group_size;  // 0 = per-channel
   int64_t G;           // number of scale rows (1 for per-channel)
@@ -45,6 +46,28 @@ struct GemvPlan {
 };
 
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size);
+
+// scale layouts the GEMV kernels tell apart
+namespace gemv {
+enum ScaleMode : int { kPerChannel = 0, kStaged = 1, kGeneric = 2 };
+}
+
+// The kernel a call runs, as launch_gemv chose it.
+struct GemvLaunch {
+  dim3 grid;
+  int R;       // rows per wave (2, 4, 8)
+  int mb;      // activation rows per workgroup (1: one-row kernel)
+  bool xl;     // activations through LDS
+  int order;   // nibble order
+  int smode;   // gemv::ScaleMode
+  bool qa4;    // dword-aligned weight rows
+  bool sa16;   // vector scale loads
+};
+
+template <typename ST>
+hipError_t launch_gemv_kernels(const GemvParams& p, const GemvLaunch& l, hipStream_t s);
+// (instantiated for float and _Float16 in q4_gemv_s32.hip / q4_gemv_s16.hip)
+
 // most activation rows one low-batch workgroup holds for this K (1: none)
 int gemv_lowbatch_max_rows(int64_t K);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
@@ -56,6 +79,7 @@ struct GemmParams {
   const uint8_t* qw;
   int64_t ldq;
   const float* scales;
+  const _Float16* scales16;  // binary16 scales instead (q4f16_1), else nullptr
   int64_t lds;
   int64_t group_size;  // 0 = per-channel
   int64_t G;

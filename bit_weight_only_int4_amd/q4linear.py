@@ -23,7 +23,7 @@ PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16", 3: "bwd_f32"}
 DTYPES = {torch.float32: 0, torch.float16: 1}
 
 # exported symbols of include/q4linear.h
-SYMBOLS = ("q4_linear", "q4_linear_workspace_bytes", "q4_linear_backward",
+SYMBOLS = ("q4_linear", "q4_linear_f16_scales", "q4_linear_workspace_bytes", "q4_linear_backward",
            "q4_linear_backward_workspace_bytes", "q4_requant", "q4_unpack_codes",
            "q4_dequant", "q4_status_str", "q4_abi_version")
 
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     P, I, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     L.q4_linear.argtypes = [P, I, P, I, P, I, I, P, P, I, I, I, I, I32, I32, P, SZ, P, P]
     L.q4_linear.restype = I32
+    L.q4_linear_f16_scales.argtypes = L.q4_linear.argtypes
+    L.q4_linear_f16_scales.restype = I32
     L.q4_linear_workspace_bytes.argtypes = [I, I, I, I, I32]
     L.q4_linear_workspace_bytes.restype = SZ
     L.q4_unpack_codes.argtypes = [P, I, I, I, I32, P, I, P]
@@ -103,22 +105,24 @@ def linear(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
            workspace: Optional[torch.Tensor] = None, return_path: bool = False):
     """out[m, n] = sum_k x[m, k] * s[g(k), n] * (q[n, k] - 8) (+ bias[n]).
 
-    x [M, K] float32; qw [N, ceil(K/2)] uint8; scales [ceil(K/gs), N] float32
-    (group_size > 0) or [N] (group_size == 0); bias [N] float32 or None.
-    Row strides of x, qw, scales and out are passed through as pitches.
+    x [M, K] float32; qw [N, ceil(K/2)] uint8; scales [ceil(K/gs), N]
+    (group_size > 0) or [N] (group_size == 0), float32, or float16 for
+    q4f16_1 weights (then q4_linear_f16_scales runs); bias [N] float32 or
+    None.  Row strides of x, qw, scales and out are passed through as pitches.
     """
     K = x.size(1) if K is None else K
     ldx = _rows(x, "x", torch.float32)
     ldq = _rows(qw, "qw", torch.uint8)
     M, N = x.size(0), qw.size(0)
+    if scales.dtype not in (torch.float32, torch.float16):
+        raise ValueError("scales must be float32 or float16")
+    entry = lib().q4_linear_f16_scales if scales.dtype == torch.float16 else lib().q4_linear
     if group_size == 0:
         if scales.dim() != 1 or scales.stride(0) != 1 or not scales.is_cuda:
             raise ValueError("per-channel scales must be a contiguous 1-D device tensor")
-        if scales.dtype != torch.float32:
-            raise ValueError("scales must be float32")
         lds = N
     else:
-        lds = _rows(scales, "scales", torch.float32)
+        lds = _rows(scales, "scales", scales.dtype)
     if bias is not None:
         if not bias.is_cuda or bias.dtype != torch.float32 or bias.dim() != 1 \
                 or bias.stride(0) != 1:
@@ -131,12 +135,12 @@ def linear(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     path = ctypes.c_int32(0)
-    st = lib().q4_linear(_ptr(x), ldx, _ptr(qw), ldq, _ptr(scales), lds, group_size,
-                         _ptr(bias), _ptr(out), ldo, M, N, K, ORDERS[nibble_order],
-                         MATHS[math], _ptr(workspace), ws_bytes, _stream(),
-                         ctypes.byref(path))
+    st = entry(_ptr(x), ldx, _ptr(qw), ldq, _ptr(scales), lds, group_size,
+               _ptr(bias), _ptr(out), ldo, M, N, K, ORDERS[nibble_order],
+               MATHS[math], _ptr(workspace), ws_bytes, _stream(),
+               ctypes.byref(path))
     if st != Q4_OK:
-        raise Q4Error(st, "q4_linear")
+        raise Q4Error(st, entry.__name__)
     return (out, PATHS[path.value]) if return_path else out
 
 

@@ -114,8 +114,34 @@ q4_status q4_linear(const float *x, int64_t ldx, const uint8_t *qw,
                     int32_t nibble_order, int32_t math, void *workspace,
                     size_t workspace_bytes, void *stream, int32_t *path_out);
 
-/* Bytes of workspace q4_linear needs for these sizes and math (0 if none).
- * Returns 0 as well for invalid sizes (q4_linear then reports the error). */
+/*
+ * q4_linear_f16_scales -- the layer with binary16 scales: the weight format
+ * that the decode kernels of page 4 ("dlight.gpu.GEMV" pull request, the
+ * WebLLM Llama-3.2-1B q4f16_1 GEMVs) run, read here as 4-bit codes with
+ * binary16 group (or per-channel) scales.  Opt-in; the layer is unchanged
+ * otherwise:
+ *
+ *   out[m, n] = sum_k x[m, k] * f32(s16[g(k), n]) * (q[n, k] - 8)  (+ bias[n])
+ *
+ * with every binary16 scale widened exactly.  Arguments, sizes, workspace,
+ * math, paths and precision are those of q4_linear, except:
+ *   scales  uint16 binary16 bit patterns, [ceil(K / group_size), lds] or [N],
+ *           2-byte aligned (the same element indexing as q4_linear)
+ * Per weight, grouped scales of 32 take 0.0625 bytes instead of 0.125.
+ * Q4_MATH_F16 feeds the same MFMA operands as q4_linear does with the
+ * widened scales (a binary16 scale is its own RN16).
+ */
+q4_status q4_linear_f16_scales(const float *x, int64_t ldx, const uint8_t *qw,
+                               int64_t ldq, const uint16_t *scales,
+                               int64_t lds, int64_t group_size,
+                               const float *bias, float *out, int64_t ldo,
+                               int64_t M, int64_t N, int64_t K,
+                               int32_t nibble_order, int32_t math,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream, int32_t *path_out);
+/* Bytes of workspace q4_linear (and q4_linear_f16_scales) needs for these
+ * sizes and math (0 if none).  Returns 0 as well for invalid sizes (the
+ * layer then reports the error). */
 size_t q4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K,
                                  int64_t group_size, int32_t math);
 

@@ -174,3 +174,22 @@ def test_backward_and_requant_validate():
         assert rq(**kw) == INVALID, kw
     assert rq(qw=LAT + 64) == ALIAS and rq(qw=S + 4) == ALIAS
     assert rq(N=0, lat=None, qw=None, scales=None) == OK
+
+
+def test_f16_scale_entry_validates():
+    """q4_linear_f16_scales: the checks of q4_linear, with 2-byte scale
+    elements (alignment and the aliasing range follow the element size)."""
+    def call16(**kw):
+        a = base_args(**kw)
+        path = ctypes.c_int32(-1)
+        st = b.lib().q4_linear_f16_scales(
+            a["x"], a["ldx"], a["qw"], a["ldq"], a["scales"], a["lds"], a["gs"], a["bias"],
+            a["out"], a["ldo"], a["M"], a["N"], a["K"], a["order"], a["math"], a["ws"],
+            a["ws_bytes"], a["stream"], ctypes.byref(path))
+        return st, path.value
+    for kw in (dict(scales=None), dict(scales=S + 1), dict(lds=127), dict(K=0),
+               dict(order=2), dict(math=5), dict(x=X + 2)):
+        assert call16(**kw) == (INVALID, 0), kw
+    # 8 groups x 128 binary16 scales end 2048 bytes after S
+    assert call16(out=S + 2044)[0] == ALIAS
+    assert call16(M=0, scales=None, x=None, qw=None, out=None) == (OK, 0)
