@@ -22,8 +22,9 @@ TFLOP/s.  `traffic` (HBM bytes per launch) comes from the committed
 rocprofv3 counter summary, and only while the HIP sources still match the
 ones it was measured on.
 
-The same run also times the four projections at a small batch (M = 4, the
-kernel the automatic choice runs), the input gradient (M = 1) and the
+The same run also times the decode step on binary16 scales (q4f16_1
+weights, q4_linear_f16_scales), the four projections at a small batch (M = 4,
+the kernel the automatic choice runs), the input gradient (M = 1) and the
 re-quantization of the four projections' weights ("backward" and "requant" objects, GB/s of
 algorithmic bytes against HBM).
 
@@ -64,19 +65,20 @@ def parse():
 class Suite:
     """Device copies of one set of projections, and graph capture of steps."""
 
-    def __init__(self, projs, torch, b, make_inputs):
+    def __init__(self, projs, torch, b, make_inputs, f16_scales=False):
         self.torch = torch
         self.b = b
         self.projs = projs
         dev = torch.device("cuda")
-        self.step_bytes = sum(p.alg_bytes() for p in projs)
+        sb = 2 if f16_scales else 4
+        self.step_bytes = sum(p.alg_bytes(sb) for p in projs)
         self.step_flops = sum(p.flops() for p in projs)
-        weight_bytes = sum(p.N * p.Kp + 4 * p.G * p.N for p in projs)
+        weight_bytes = sum(p.N * p.Kp + sb * p.G * p.N for p in projs)
         self.copies = max(2, -(-ROTATE_BYTES // weight_bytes))
         self.items = []
         for p in projs:
             x, qw, s, bias = make_inputs(p, 0)
-            qd, sd = qw.to(dev), s.to(dev)
+            qd, sd = qw.to(dev), (s.half() if f16_scales else s).to(dev)
             qs = [qd] + [qd.clone() for _ in range(self.copies - 1)]
             ss = [sd] + [sd.clone() for _ in range(self.copies - 1)]
             out = torch.empty((p.M, p.N), dtype=torch.float32, device=dev)
@@ -395,6 +397,30 @@ def main():
         del dec
         torch.cuda.empty_cache()
 
+    if args.only in ("decode", "both"):
+        # the same decode step on q4f16_1 weights (binary16 scales)
+        print("[bench] decode, binary16 scales", file=sys.stderr, flush=True)
+        d16 = Suite(dec_projs, torch, b, make_inputs, f16_scales=True)
+        m = measure(d16, max(16, args.steps // 4), max(4, args.warmup // 4), torch)
+        times = launch_times(d16, torch)
+        ach = d16.step_bytes / sum(times) / 1e9
+        result["decode_f16_scales"] = dict(
+            value=round(d16.step_bytes / (m["ms_per_step"] / 1e3) / 1e9, 1), unit="GB/s",
+            ms_per_step=round(m["ms_per_step"], 6), steps=m["steps"],
+            alg_bytes_per_step=d16.step_bytes, rotating_weight_copies=d16.copies,
+            config={"workload": "decode_1b projections, scales rounded to binary16 "
+                                "(q4_linear_f16_scales)"},
+            roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                          kernel="gemv_f32, binary16 scales (all four projections)",
+                          avg_launch_us=round(sum(times) / len(times) * 1e6, 3)),
+            per_projection_us=[(dec_projs[i].name, round(t * 1e6, 3))
+                               for i, t in enumerate(times)])
+        print(f"[bench] binary16 scales done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
+        del d16
+        torch.cuda.empty_cache()
+
     if args.only in ("decode", "both") and args.lowbatch_m > 1:
         lb_projs = [p.with_m(args.lowbatch_m) for p in dec_projs]
         print(f"[bench] small batch M={args.lowbatch_m}", file=sys.stderr, flush=True)
@@ -492,6 +518,8 @@ def main():
             "roofline": pf["roofline"],
             "per_projection_us_tflops": pf["per_proj"],
         }
+    if "decode_f16_scales" in result:
+        line["decode_f16_scales"] = result["decode_f16_scales"]
     if "lowbatch" in result:
         line["lowbatch"] = result["lowbatch"]
     for kind, what in (("backward", "input gradient dx = dout . dequant(W), M=1"),

@@ -49,9 +49,10 @@ class Projection:
         return replace(self, M=M, name=f"{self.name.split('@')[0]}@M{M}")
 
     # Algorithmic HBM bytes of one call: packed weights, scales, x, out, bias.
-    def alg_bytes(self) -> int:
+    def alg_bytes(self, scale_bytes: int = 4) -> int:
+        """scale_bytes: 4 for fp32 scales, 2 for binary16 (q4f16_1)."""
         scale_elems = self.N if self.group_size == 0 else self.G * self.N
-        b = self.N * self.Kp + 4 * scale_elems + 4 * self.M * self.K \
+        b = self.N * self.Kp + scale_bytes * scale_elems + 4 * self.M * self.K \
             + 4 * self.M * self.N
         if self.has_bias:
             b += 4 * self.N
