@@ -237,12 +237,20 @@ __device__ __forceinline__ void gemv_tile(const GemvParams& p, int64_t m, int64_
   }
   if (XL) {
     static_assert(!XL || CPL == 1, "activations in LDS: one chunk per lane");
-    // Wait for every load in flight: the activation loads and the scale and
-    // weight loads above, issued together, so the wait is about one memory
-    // latency.  (A partial count would depend on how the compiler merges
-    // adjacent loads.)
+    // Wait for the activation loads only (the kernel issued them before the
+    // scale and weight loads, and vector memory operations retire in
+    // order): vmcnt may still count the loads issued after them.  Interior
+    // tiles of aligned rows issue exactly one 16-byte load per weight row
+    // (rows lie ldq bytes apart, so none merge) and, for fp32 scales, one
+    // 16-byte scale load per four rows; counting fewer than were issued only
+    // waits longer, so binary16 and scalar scale loads, which the compiler
+    // may merge, are not counted.  Each row's arithmetic then waits for its
+    // own load alone (the compiler's wait), so the first rows are computed
+    // while the later ones are still arriving.
+    constexpr int NEWER =
+        (!GUARD && QA4) ? R + ((SMODE == kStaged && SA16 && sizeof(ST) == 4) ? R / 4 : 0) : 0;
     asm volatile("" ::: "memory");
-    wait_vmcnt<0>();
+    wait_vmcnt<NEWER>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
