@@ -24,7 +24,8 @@ ones it was measured on.
 
 The same run also times the decode step on binary16 scales (q4f16_1
 weights, q4_linear_f16_scales), the four projections at a small batch (M = 4,
-the kernel the automatic choice runs), the input gradient (M = 1) and the
+the kernel the automatic choice runs), the input gradient (M = 1, and at the
+prefill size on MFMA) and the
 re-quantization of the four projections' weights ("backward" and "requant" objects, GB/s of
 algorithmic bytes against HBM).
 
@@ -129,10 +130,11 @@ class TrainSuite:
     for the gradient, fp32 latents for re-quantization) so that each launch
     reads it from HBM."""
 
-    def __init__(self, projs, torch, b, make_inputs, kind):
+    def __init__(self, projs, torch, b, make_inputs, kind, M=1):
         self.torch = torch
         self.b = b
         self.kind = kind
+        self.step_flops = sum(2 * M * p.N * p.K for p in projs)
         dev = torch.device("cuda")
         self.items = []
         per_step = 0
@@ -150,11 +152,11 @@ class TrainSuite:
             it = dict(p=p, s=sd)
             if kind == "backward":
                 it["q"] = [qw.to(dev) for _ in range(self.copies)]
-                it["dout"] = torch.randn((1, p.N), generator=g).to(dev)
-                it["dx"] = torch.empty((1, p.K), device=dev)
-                need = b.backward_workspace_bytes(1, p.N, p.K, p.group_size)
+                it["dout"] = torch.randn((M, p.N), generator=g).to(dev)
+                it["dx"] = torch.empty((M, p.K), device=dev)
+                need = b.backward_workspace_bytes(M, p.N, p.K, p.group_size)
                 it["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-                self.step_bytes += p.N * p.Kp + 4 * p.G * p.N + 4 * p.N + 4 * p.K
+                self.step_bytes += p.N * p.Kp + 4 * p.G * p.N + 4 * M * p.N + 4 * M * p.K
             else:
                 w = b.dequant(qw.to(dev), sd, p.K, p.group_size, p.order, torch.float32)
                 it["lat"] = [w.clone() for _ in range(self.copies)]
@@ -179,10 +181,28 @@ class TrainSuite:
     kernel_graph = Suite.kernel_graph
 
 
-def train_measure(kind, projs, torch, b, make_inputs, steps, warmup):
-    suite = TrainSuite(projs, torch, b, make_inputs, kind)
+def train_measure(kind, projs, torch, b, make_inputs, steps, warmup, M=1):
+    suite = TrainSuite(projs, torch, b, make_inputs, kind, M)
     m = measure(suite, steps, warmup, torch)
     times = launch_times(suite, torch)
+    if M > 1:
+        # the prefill-sized input gradient: binary16 operands on MFMA
+        tf = suite.step_flops / (m["ms_per_step"] / 1e3) / 1e12
+        ach = suite.step_flops / sum(times) / 1e12
+        res = dict(
+            value=round(tf, 2), unit="TFLOP/s", ms_per_step=round(m["ms_per_step"], 6),
+            steps=m["steps"], flops_per_step=suite.step_flops,
+            rotating_copies=suite.copies,
+            roofline=dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
+                          unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                          traffic=None,
+                          kernel="dout16 + bwd_mfma (+ split-N reduce), per call",
+                          avg_launch_us=round(sum(times) / len(times) * 1e6, 3)),
+            per_projection_us=[(p.with_m(M).name, round(t * 1e6, 3))
+                               for p, t in zip(projs, times)])
+        del suite
+        torch.cuda.empty_cache()
+        return res
     gbs = suite.step_bytes / (m["ms_per_step"] / 1e3) / 1e9
     ach = suite.step_bytes / sum(times) / 1e9
     res = dict(
@@ -481,6 +501,13 @@ def main():
                                          max(16, args.steps // 4), max(4, args.warmup // 4))
             print(f"[bench] {kind} done: {result[kind]['ms_per_step']:.4f} ms/step",
                   file=sys.stderr, flush=True)
+        print(f"[bench] backward at M={args.prefill_m}", file=sys.stderr, flush=True)
+        result["backward_prefill"] = train_measure(
+            "backward", dec_projs, torch, b, make_inputs, max(8, args.steps // 16),
+            max(2, args.warmup // 8), M=args.prefill_m)
+        print(f"[bench] backward at M={args.prefill_m} done: "
+              f"{result['backward_prefill']['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
 
     cpu = None
     if not args.no_cpu_baseline and "decode" in result:
@@ -523,6 +550,8 @@ def main():
     if "lowbatch" in result:
         line["lowbatch"] = result["lowbatch"]
     for kind, what in (("backward", "input gradient dx = dout . dequant(W), M=1"),
+                       ("backward_prefill", "input gradient at M=%d (automatic choice: "
+                        "binary16 operands on MFMA)" % args.prefill_m),
                        ("requant", "re-quantization of fp32 latents into packed codes")):
         if kind in result:
             r = result[kind]

@@ -56,6 +56,22 @@ int32_t resolve_math(int32_t math, int64_t M, int64_t N, int64_t K, int64_t grou
   return Q4_MATH_F16;
 }
 
+// The MFMA input gradient applies one scale per packed word: per-channel
+// scales, or groups that are whole words.
+bool bwd_mfma_groups(int64_t K, int64_t group_size) {
+  return group_size == 0 || group_size >= K || group_size % 8 == 0;
+}
+
+// Arithmetic of the input gradient.  Q4_MATH_AUTO, as for the forward:
+// fp32 for few activation rows, binary16 operands on MFMA from 16 rows on
+// (measured faster there on MI355X, 7x at 512 rows) when the groups allow
+// it.  Sizes only, so the workspace query and the call agree.
+int32_t resolve_bwd_math(int32_t math, int64_t M, int64_t N, int64_t K, int64_t group_size) {
+  (void)N;
+  if (math != Q4_MATH_AUTO) return math;
+  return (M >= 16 && bwd_mfma_groups(K, group_size)) ? Q4_MATH_F16 : Q4_MATH_F32;
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,8 +213,10 @@ size_t q4_linear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int64
   if (M <= 0 || N <= 0 || K <= 0 || group_size < 0 || M >= kMaxDim || N >= kMaxDim ||
       K >= kMaxDim)
     return 0;
-  if (math != Q4_MATH_AUTO && math != Q4_MATH_F32) return 0;
-  return q4::bwd_workspace_bytes(M, N, K);
+  const int32_t m = resolve_bwd_math(math, M, N, K, group_size);
+  if (m == Q4_MATH_F32) return q4::bwd_workspace_bytes(M, N, K);
+  if (m == Q4_MATH_F16) return q4::bwd_mfma_workspace_bytes(M, N, K);
+  return 0;
 }
 
 q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw, int64_t ldq,
@@ -217,7 +235,8 @@ q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw,
   const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
   if (lddo < N || ldq < Kp || lddx < K) return Q4_ERR_INVALID_ARG;
   if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
-  if (math == Q4_MATH_F16) return Q4_ERR_UNSUPPORTED;
+  const int32_t m = resolve_bwd_math(math, M, N, K, group_size);
+  if (m == Q4_MATH_F16 && !bwd_mfma_groups(K, group_size)) return Q4_ERR_UNSUPPORTED;
   if (M == 0) return Q4_OK;
   if (!dout || !qw || !scales || !dx) return Q4_ERR_INVALID_ARG;
   if (!aligned(dout, 4) || !aligned(scales, 4) || !aligned(dx, 4)) return Q4_ERR_INVALID_ARG;
@@ -226,7 +245,7 @@ q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw,
   const Range r_q = span(qw, N, ldq, Kp, 1);
   const Range r_s = group_size == 0 ? span(scales, 1, N, N, 4) : span(scales, G, lds, N, 4);
   if (overlap(r_dx, r_do) || overlap(r_dx, r_q) || overlap(r_dx, r_s)) return Q4_ERR_ALIAS;
-  const size_t need = q4::bwd_workspace_bytes(M, N, K);
+  const size_t need = q4_linear_backward_workspace_bytes(M, N, K, group_size, m);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return Q4_ERR_WORKSPACE;
@@ -241,9 +260,15 @@ q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw,
   p.dx = dx; p.lddx = lddx; p.partial = reinterpret_cast<float*>(workspace);
   p.M = M; p.N = N; p.K = K;
   const bool qa4 = aligned(qw, 4) && (ldq % 4 == 0);
-  const hipError_t e =
-      q4::launch_bwd_f32(p, nibble_order, qa4, reinterpret_cast<hipStream_t>(stream));
-  if (path_out) *path_out = Q4_PATH_BWD_F32;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (m == Q4_MATH_F16) {
+    e = q4::launch_bwd_mfma(p, nibble_order, qa4, workspace, st);
+    if (path_out) *path_out = Q4_PATH_BWD_F16;
+  } else {
+    e = q4::launch_bwd_f32(p, nibble_order, qa4, st);
+    if (path_out) *path_out = Q4_PATH_BWD_F32;
+  }
   return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
 }
 

@@ -293,9 +293,9 @@ gemv_f32_kernel(const GemvParams p) {
   constexpr int SPAN = 64 * CPL * 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // wave = wk * WR + wr; WR (row groups) is 1, 2 or 4
+  // wave = wk * WR + wr; WR (row groups) is a power of two
   const int WK = p.waves_k, WR = p.waves_r, W = WK * WR;
-  const int lwr = WR == 4 ? 2 : WR == 2 ? 1 : 0;
+  const int lwr = 31 - __builtin_clz(WR);
   const int wr = wave & (WR - 1), wk = wave >> lwr;
   const int64_t m = blockIdx.y;
   const int z = blockIdx.z;
@@ -376,9 +376,9 @@ gemv_lb_kernel(const GemvParams p) {
   constexpr int SPAN = 2048;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // wave = wk * WR + wr; WR (row groups) is 1, 2 or 4
+  // wave = wk * WR + wr; WR (row groups) is a power of two
   const int WK = p.waves_k, WR = p.waves_r, W = WK * WR;
-  const int lwr = WR == 4 ? 2 : WR == 2 ? 1 : 0;
+  const int lwr = 31 - __builtin_clz(WR);
   const int wr = wave & (WR - 1), wk = wave >> lwr;
   const int64_t m0 = (int64_t)blockIdx.y * MB;
   const int z = blockIdx.z;

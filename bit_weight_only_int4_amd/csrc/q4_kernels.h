@@ -149,6 +149,37 @@ hipError_t launch_requant(const float* latent, int64_t ldl, const float* scales,
                           int64_t gs, int64_t N, int64_t K, int order, uint8_t* qw, int64_t ldq,
                           hipStream_t s);
 
+// input gradient on MFMA (binary16 operands, fp32 accumulation)
+struct BwdMfmaParams {
+  const _Float16* d16;  // binary16 d_out [mp][np] (workspace), zero-padded
+  int64_t d16_pitch;
+  const uint8_t* qw;
+  int64_t ldq;
+  const float* scales;
+  int64_t lds;
+  int64_t group_size;  // 0 = per-channel; else a multiple of 8
+  int32_t log2_gs;     // power-of-two group size: log2, else -1
+  float* dx;
+  int64_t lddx;
+  float* partial;      // [split][M][K] when split > 1 (workspace)
+  int64_t M, N, K;
+  int64_t n_per_split; // multiple of the N step
+  int32_t split;
+  int32_t tiles_m, tiles_k;
+};
+
+struct BwdMfmaPlan {
+  int64_t tiles_m, tiles_k;
+  int64_t mp, np;      // padded binary16 d_out
+  int64_t n_per_split;
+  int split;
+};
+
+BwdMfmaPlan plan_bwd_mfma(int64_t M, int64_t N, int64_t K);
+size_t bwd_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_bwd_mfma(const BwdParams& p, int order, bool qa4, void* workspace,
+                           hipStream_t s);
+
 // out[m, n] = sum over z of partial[z][m][n] (+ bias[n]), z in order
 hipError_t launch_splitk_reduce(const float* partial, const float* bias, float* out, int64_t ldo,
                                 int64_t M, int64_t N, int split, hipStream_t s);

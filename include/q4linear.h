@@ -72,6 +72,7 @@ typedef int32_t q4_status;
 #define Q4_PATH_GEMV_F32 1  /* streaming fp32 GEMV, activation rows 1..M */
 #define Q4_PATH_GEMM_F16 2  /* MFMA f16 x f16 -> f32 GEMM */
 #define Q4_PATH_BWD_F32 3   /* fp32 input gradient (q4_linear_backward) */
+#define Q4_PATH_BWD_F16 4   /* MFMA f16 x f16 -> f32 input gradient */
 
 /* Element type of q4_dequant's output. */
 #define Q4_DTYPE_F32 0
@@ -166,18 +167,27 @@ q4_status q4_unpack_codes(const uint8_t *qw, int64_t ldq, int64_t N,
  *   dout    float [M, lddo]       lddo >= N
  *   qw, ldq, scales, lds, group_size, nibble_order: as in q4_linear
  *   dx      float [M, lddx]       lddx >= K; must not overlap any input
- *   math    Q4_MATH_AUTO or Q4_MATH_F32 (pure fp32: the weight is applied as
- *           c * RN32(dout * s) when a packed word lies in one group, else
- *           as RN32(c * s); fp32 sums); Q4_MATH_F16 is Q4_ERR_UNSUPPORTED
+ *   math    Q4_MATH_AUTO: F16 when M >= 16 and the group size allows it,
+ *           else F32 (decided on sizes alone).
+ *           Q4_MATH_F32: pure fp32 (the weight is applied
+ *           as c * RN32(dout * s) when a packed word lies in one group, else
+ *           as RN32(c * s); fp32 sums), path Q4_PATH_BWD_F32.
+ *           Q4_MATH_F16: binary16 operands on MFMA, fp32 sums: RN16(dout)
+ *           times w = RN16(c * RN16(s)) (the forward F16 path's weight
+ *           operand), path Q4_PATH_BWD_F16; needs group_size == 0,
+ *           group_size >= K or group_size % 8 == 0, else
+ *           Q4_ERR_UNSUPPORTED.
  *   workspace     device scratch of q4_linear_backward_workspace_bytes(...)
- *                 bytes (partial sums over row blocks of the weight), may be
- *                 NULL when that is 0; contents on entry ignored, on exit
+ *                 bytes for the same math (F32: partial sums over row blocks
+ *                 of the weight; F16: binary16 dout and split partials), may
+ *                 be NULL when that is 0; contents on entry ignored, on exit
  *                 undefined
- *   stream, path_out: as in q4_linear (path Q4_PATH_BWD_F32)
+ *   stream, path_out: as in q4_linear
  *
  * Sizes are validated as in q4_linear (K > 0).  M == 0 is a no-op; N == 0
  * (an empty contraction) is Q4_ERR_INVALID_ARG.
- * Precision: max |dx - exact| / sum_n |dout * w| about 1e-5 or better.
+ * Precision: max |dx - exact| / sum_n |dout * w| about 1e-5 or better for
+ * F32, under 2e-3 for F16.
  */
 q4_status q4_linear_backward(const float *dout, int64_t lddo, const uint8_t *qw,
                              int64_t ldq, const float *scales, int64_t lds,
@@ -186,7 +196,8 @@ q4_status q4_linear_backward(const float *dout, int64_t lddo, const uint8_t *qw,
                              int32_t math, void *workspace, size_t workspace_bytes,
                              void *stream, int32_t *path_out);
 
-/* Bytes of workspace q4_linear_backward needs (0 if none, or invalid sizes). */
+/* Bytes of workspace q4_linear_backward needs for these sizes and math (0 if
+ * none, or invalid sizes). */
 size_t q4_linear_backward_workspace_bytes(int64_t M, int64_t N, int64_t K,
                                           int64_t group_size, int32_t math);
 

@@ -152,7 +152,12 @@ def test_backward_and_requant_validate():
                dict(ldq=127), dict(lds=127), dict(lddx=255), dict(order=2), dict(math=5),
                dict(dout=DO + 2), dict(dx=DX + 1)):
         assert bwd(**kw) == INVALID, kw
-    assert bwd(math=2) == 4  # binary16 backward is not part of this build
+    # the MFMA backward needs one scale per packed word, and always a workspace
+    # (binary16 dout)
+    assert bwd(math=2, gs=3, lds=128) == 4
+    assert bwd(math=2, gs=20) == 4
+    assert bwd(math=2) == WORKSPACE
+    assert L.q4_linear_backward_workspace_bytes(2, 128, 256, 32, 2) >= 128 * 128 * 2
     for dx in (DO, Q + 8, S):
         assert bwd(dx=dx) == ALIAS
     assert bwd(M=0, dout=None, dx=None) == OK
@@ -160,7 +165,6 @@ def test_backward_and_requant_validate():
     assert L.q4_linear_backward_workspace_bytes(2, 128, 256, 32, 0) == 0
     assert L.q4_linear_backward_workspace_bytes(2, 1024, 256, 32, 0) > 0
     assert bwd(N=1024, lddo=1024, lds=1024) == WORKSPACE
-    assert L.q4_linear_backward_workspace_bytes(2, 128, 256, 32, 2) == 0
 
     def rq(**kw):
         a = dict(lat=LAT, ldl=256, scales=S, lds=128, gs=32, N=128, K=256, order=0, qw=Q,

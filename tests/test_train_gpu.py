@@ -4,9 +4,10 @@
     (clamp(round(latent / s), -8, 7) + 8, ties to even, zero scale -> 8), on
     latents that mix in-range values, exact ties, clamped magnitudes, zero
     scales, infinities and NaN; bytes past ceil(K/2) stay untouched.
-  * q4_linear_backward: dx = dout . dequant(W) within 1e-5 of the fp64
-    oracle, normalised by sum_n |dout * w| (exact where that is 0), with
-    NaN-poisoned outputs, guard slots and padded pitches.
+  * q4_linear_backward: dx = dout . dequant(W) within 1e-5 (fp32 path) or
+    2e-3 (binary16 operands on MFMA) of the fp64 oracle, normalised by
+    sum_n |dout * w| (exact where that is 0), with NaN-poisoned outputs,
+    guard slots and padded pitches.
 Page 3, "Add fp32 matmul ops (mm, bmm, linear)", stack entries #20943,
 #20945 and #20946.
 """
@@ -23,6 +24,9 @@ from tests.gpu_util import log, need_gpu, normalised_error
 from tests.packing import pack
 
 pytestmark = pytest.mark.gpu
+
+# fp32 path; binary16 operands on MFMA with fp32 sums (the forward's bars)
+BWD_TOL = {"bwd_f32": 1e-5, "bwd_f16": 2e-3}
 
 
 def _scales(rng, N, K, gs, lo=0.005, hi=0.02):
@@ -104,8 +108,9 @@ def test_requant_round_trip_through_dequant():
         assert np.array_equal(back.cpu().numpy(), qw)
 
 
-def _bwd_case(M, N, K, gs, order, *, pad=(0, 0, 0, 0), seed=0, all_eights=False):
-    log(f"[backward] M={M} N={N} K={K} gs={gs} order={order} pad={pad}")
+def _bwd_case(M, N, K, gs, order, *, pad=(0, 0, 0, 0), seed=0, all_eights=False,
+              math="auto"):
+    log(f"[backward] M={M} N={N} K={K} gs={gs} order={order} pad={pad} math={math}")
     rng = np.random.default_rng(seed)
     raw = np.full((N, K), 8) if all_eights else rng.integers(0, 16, (N, K))
     qw = pack(raw, order, pad=int(rng.integers(0, 16)))
@@ -128,16 +133,18 @@ def _bwd_case(M, N, K, gs, order, *, pad=(0, 0, 0, 0), seed=0, all_eights=False)
     dbuf = torch.full((M + 2, K + pad[3]), float("nan"), dtype=torch.float32, device=dev)
     dx = dbuf[:M, :K]
     _, path = b.linear_backward(dd, qd, sd, K=K, group_size=gs, nibble_order=order, dx=dx,
-                                return_path=True)
+                                math=math, return_path=True)
     torch.cuda.synchronize()
     full = dbuf.cpu().numpy()
-    assert path == "bwd_f32"
+    auto_f16 = M >= 16 and (gs == 0 or gs >= K or gs % 8 == 0)
+    assert path == ("bwd_f16" if math == "f16" or (math == "auto" and auto_f16) else "bwd_f32")
+    tol = BWD_TOL[path]
     assert np.all(np.isnan(full[M:, :])) and np.all(np.isnan(full[:M, K:])), "guard written"
     got = full[:M, :K]
     assert not np.any(np.isnan(got))
     err = normalised_error(got, ref, den)
-    log(f"          max normalised error={err:.3e} (tol 1e-05)")
-    assert err <= 1e-5
+    log(f"          path={path} max normalised error={err:.3e} (tol {tol:.0e})")
+    assert err <= tol
     return got
 
 
@@ -159,7 +166,8 @@ def test_backward_parity(M, N, K, gs, order, pad):
 
 
 def test_backward_prefill_sized_sampled():
-    """M = 512 over a 1B-shaped weight, checked on sampled elements."""
+    """M = 512 over a 1B-shaped weight on the fp32 path, checked on sampled
+    elements."""
     need_gpu()
     rng = np.random.default_rng(512)
     M, N, K, gs = 512, 2048, 2048, 32
@@ -168,7 +176,7 @@ def test_backward_prefill_sized_sampled():
     dout = rng.standard_normal((M, N)).astype(np.float32)
     dev = torch.device("cuda")
     got = b.linear_backward(torch.from_numpy(dout).to(dev), torch.from_numpy(qw).to(dev),
-                            torch.from_numpy(scales).to(dev), K=K, group_size=gs)
+                            torch.from_numpy(scales).to(dev), K=K, group_size=gs, math="f32")
     torch.cuda.synchronize()
     ms = rng.integers(0, M, 400)
     ks = rng.integers(0, K, 400)
@@ -224,3 +232,66 @@ def test_backward_full_size_sampled(name):
         err = normalised_error(got.cpu().numpy()[0, ks], ref, den)
         log(f"          max normalised error={err:.3e}")
         assert err <= 1e-5
+
+
+# ---- the MFMA input gradient (math="f16") ---------------------------------
+@pytest.mark.parametrize("M,N,K,gs,order,pad", [
+    (1, 515, 2048, 32, "low_first", (0, 0, 0, 0)),
+    (2, 300, 1000, 8, "high_first", (0, 0, 0, 0)),
+    (33, 256, 300, 24, "low_first", (1, 2, 3, 4)),
+    (128, 2048, 512, 128, "high_first", (0, 0, 0, 0)),
+    (130, 1000, 2008, 0, "high_first", (0, 1, 0, 0)),
+    (70, 4096, 1024, 32, "low_first", (0, 0, 0, 0)),
+    (257, 640, 2007, 32, "low_first", (3, 4, 1, 5)),
+    (64, 77, 129, 16, "high_first", (0, 3, 0, 0)),
+    (5, 3, 1, 0, "low_first", (0, 0, 0, 0)),
+])
+def test_backward_f16_parity(M, N, K, gs, order, pad):
+    need_gpu()
+    _bwd_case(M, N, K, gs, order, pad=pad, seed=M * 977 + N + K, math="f16")
+
+
+def test_backward_f16_all_eights_and_determinism():
+    need_gpu()
+    got = _bwd_case(40, 700, 1024, 32, "low_first", seed=4, all_eights=True, math="f16")
+    assert np.all(got == 0)
+    rng = np.random.default_rng(10)
+    M, N, K, gs = 96, 4096, 2048, 32
+    dev = torch.device("cuda")
+    qw = torch.from_numpy(pack(rng.integers(0, 16, (N, K)))).to(dev)
+    scales = torch.from_numpy(_scales(rng, N, K, gs)).to(dev)
+    dout = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(dev)
+    a = b.linear_backward(dout, qw, scales, K=K, group_size=gs, math="f16")
+    c = b.linear_backward(dout, qw, scales, K=K, group_size=gs, math="f16")
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("name", ["prefill_1b", "llama8b_gs128"])
+def test_backward_f16_full_size_sampled(name):
+    """Every projection at M = 512 over full-size weights, on 400 sampled
+    gradient elements computed one by one by the oracle."""
+    need_gpu()
+    from bit_weight_only_int4_amd.workloads import make_inputs
+    dev = torch.device("cuda")
+    for p in CONFIGS[name]:
+        if p.M != 512:
+            continue
+        seed = zlib.crc32(p.name.encode())
+        log(f"[backward f16 full] {p.name} seed={seed}")
+        _, qw, scales, _ = make_inputs(p, seed)
+        g = torch.Generator().manual_seed(seed + 1)
+        dout = torch.randn((p.M, p.N), generator=g)
+        got, path = b.linear_backward(dout.to(dev), qw.to(dev), scales.to(dev), K=p.K,
+                                      group_size=p.group_size, nibble_order=p.order,
+                                      math="f16", return_path=True)
+        torch.cuda.synchronize()
+        assert path == "bwd_f16"
+        rng = np.random.default_rng(seed)
+        ms = rng.integers(0, p.M, 400)
+        ks = rng.integers(0, p.K, 400)
+        ref, den = orc.linear_backward_sampled(dout.numpy(), qw.numpy(), scales.numpy(), ms, ks,
+                                               K=p.K, group_size=p.group_size, order=p.order)
+        err = normalised_error(got.cpu().numpy()[ms, ks], ref, den)
+        log(f"          max normalised error={err:.3e}")
+        assert err <= BWD_TOL["bwd_f16"]
