@@ -234,11 +234,12 @@ BwdMfmaPlan plan_bwd_mfma(int64_t M, int64_t N, int64_t K) {
   pl.mp = pl.tiles_m * BB_M;
   const int64_t steps = (N + BB_S - 1) / BB_S;
   pl.np = steps * BB_S;
-  // split N while the tiles alone leave CUs without 4 workgroups and each
-  // split keeps at least 16 steps
+  // split N while the tiles alone leave CUs without 2 workgroups (the LDS
+  // holds two) and each split keeps at least 4 steps (measured best of
+  // several such rules over M = 16 .. 2048)
   const int64_t tiles = pl.tiles_m * pl.tiles_k;
   int64_t split = 1;
-  while (tiles * split * 2 <= 1024 && steps / (split * 2) >= 16) split *= 2;
+  while (tiles * split * 2 <= 512 && steps / (split * 2) >= 4) split *= 2;
   const int64_t per = (steps + split - 1) / split;
   pl.n_per_split = per * BB_S;
   pl.split = (int)((N + pl.n_per_split - 1) / pl.n_per_split);
