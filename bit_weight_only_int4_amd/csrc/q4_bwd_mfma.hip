@@ -39,6 +39,9 @@ constexpr int BB_K = 128;     // output columns k per tile
 constexpr int BB_S = 64;      // contraction step over n (32 or 64; 64 measured
                               // faster from 512 rows on)
 constexpr int BB_NT = 256;
+// row pitch, in floats, of the output tile the epilogue stages in LDS (the
+// two row halves of one LDS store land on disjoint banks)
+constexpr int BB_EPI_TP = 136;
 // LDS row pitch in halves: NS + 8 (80 or 144 bytes), so the 16 rows that
 // one 16-lane group of a ds_read_b128 reads fall on 16 distinct 4-bank
 // groups
@@ -67,8 +70,15 @@ bwd_mfma_kernel(const BwdMfmaParams p) {
   constexpr int PITCH = bb_pitch<NS>();
   constexpr int AP = NS / 16;  // 16-byte d_out pieces per thread per step
   constexpr int BP = NS / 32;  // row pairs per thread per step
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BB_M * PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BB_K * PITCH];
+  struct Smem {
+    _Float16 a[2][BB_M * PITCH];
+    _Float16 b[2][BB_K * PITCH];
+  };
+  static_assert(sizeof(Smem) >= BB_M * BB_EPI_TP * sizeof(float),
+                "the epilogue stages the output tile in the operand buffers");
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  auto& As = sm.a;
+  auto& Bs = sm.b;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -197,21 +207,49 @@ bwd_mfma_kernel(const BwdMfmaParams p) {
     __syncthreads();
   }
 
-  // epilogue: lane l, element v of a 32x32 block holds row
-  // 8 * (v / 4) + 4 * (l / 32) + v % 4 and column l % 32
-  const int64_t col = k0 + 32 * w + li;
-  if (col >= p.K) return;
+  // Epilogue (the loop's last barrier has freed the operand buffers): the
+  // tile goes through LDS and leaves as 16-byte row-contiguous stores,
+  // non-temporal for d_x.  Lane l, element v of a 32x32 block holds row
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4 and column l % 32.
+  float* ctile = reinterpret_cast<float*>(&sm);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * lb + (v & 3);
-      if (row >= p.M) continue;
+    for (int v = 0; v < 16; ++v)
+      ctile[(32 * i + 8 * (v >> 2) + 4 * lb + (v & 3)) * BB_EPI_TP + 32 * w + li] = acc[i][v];
+  __syncthreads();
+  const int c4 = tid & 31;  // column quad of the tile
+  const int64_t col = k0 + 4 * c4;
+  float* dst0;
+  int64_t pitch;
+  bool vec;
+  if (p.split > 1) {
+    dst0 = p.partial + (int64_t)z * p.M * p.K;
+    pitch = p.K;
+    vec = p.K % 4 == 0 && reinterpret_cast<uintptr_t>(dst0) % 16 == 0;
+  } else {
+    dst0 = p.dx;
+    pitch = p.lddx;
+    vec = p.lddx % 4 == 0 && reinterpret_cast<uintptr_t>(p.dx) % 16 == 0;
+  }
+#pragma unroll 4
+  for (int j = 0; j < BB_M / 8; ++j) {
+    const int r = (tid >> 5) + 8 * j;
+    const int64_t row = m0 + r;
+    if (row >= p.M) break;
+    const f4 v = *reinterpret_cast<const f4*>(ctile + r * BB_EPI_TP + 4 * c4);
+    float* dst = dst0 + row * pitch + col;
+    if (vec && col + 4 <= p.K) {
       if (p.split > 1)
-        p.partial[((int64_t)z * p.M + row) * p.K + col] = acc[i][v];
+        *reinterpret_cast<f4*>(dst) = v;
       else
-        p.dx[row * p.lddx + col] = acc[i][v];
+        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(dst));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.K) dst[e] = v[e];
     }
+  }
 }
 
 template <int ORDER>

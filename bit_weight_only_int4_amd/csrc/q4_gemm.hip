@@ -399,6 +399,9 @@ constexpr int PIPE_NT = 256;
 // 16-lane group of a ds_read_b128 touches on 16 distinct 4-bank groups.
 __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+// row pitch, in floats, of the output tile the epilogue stages in LDS
+constexpr int EPI_TP = 136;
+
 template <int NSTAGE>
 struct PipeSmem {
   uint32_t a[NSTAGE][BM * KS / 2];       // binary16 activations, swizzled
@@ -415,6 +418,8 @@ __global__ void __launch_bounds__(PIPE_NT)
 gemm_pipe_kernel(const GemmParams p) {
   static_assert(NSTAGE >= 3 && NSTAGE <= 6, "pipeline depth");
   static_assert(6 * (NSTAGE - 1) < 64, "vmcnt range");
+  static_assert(sizeof(PipeSmem<NSTAGE>) >= BM * EPI_TP * sizeof(float),
+                "the epilogue stages the output tile in the pipeline's LDS");
   __shared__ __attribute__((aligned(16))) PipeSmem<NSTAGE> sm;
 
   const int tid = threadIdx.x;
@@ -570,22 +575,63 @@ gemm_pipe_kernel(const GemmParams p) {
   }
   wait_vm_lgkm0<0>();
 
-  // epilogue: lane l, element v of a 32x32 block holds row
-  // 8*(v/4) + 4*(l/32) + v%4 and column l%32
-  const int64_t col = n0 + 32 * w + li;
-  if (col < p.N) {
-    const float bcolv = (p.split == 1 && p.bias) ? p.bias[col] : 0.0f;
+  // Epilogue.  Every wave's loads have landed and its LDS reads are done, so
+  // the ring is free: the tile goes through LDS and leaves as 16-byte
+  // row-contiguous stores (a wave writes two 512-byte row segments per
+  // store), non-temporal for the output, which nothing here reads again.
+  // The output write is the one serial phase after the MFMA loop; 4-byte
+  // stores straight from the MFMA layout (two 128-byte segments per store)
+  // measured about 1.5x slower at M = 512.
+  // Lane l, element v of a 32x32 block holds row 8*(v/4) + 4*(l/32) + v%4
+  // and column l%32; the row pitch (EPI_TP floats) puts the two row halves
+  // of one LDS store on disjoint banks.
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  float* ctile = reinterpret_cast<float*>(&sm);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3);
-        if (row >= p.M) continue;
-        if (p.split > 1)
-          p.partial[((int64_t)z * p.M + row) * p.N + col] = acc[i][v];
-        else
-          p.out[row * p.ldo + col] = acc[i][v] + bcolv;
-      }
+    for (int v = 0; v < 16; ++v)
+      ctile[(i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3)) * EPI_TP + 32 * w + li] = acc[i][v];
+  __syncthreads();
+  const int c4 = tid & 31;  // column quad of the tile
+  const int64_t col = n0 + 4 * c4;
+  float* dst0;
+  int64_t pitch;
+  bool vec;
+  if (p.split > 1) {
+    dst0 = p.partial + (int64_t)z * p.M * p.N;
+    pitch = p.N;
+    vec = p.N % 4 == 0 && reinterpret_cast<uintptr_t>(dst0) % 16 == 0;
+  } else {
+    dst0 = p.out;
+    pitch = p.ldo;
+    vec = p.ldo % 4 == 0 && reinterpret_cast<uintptr_t>(p.out) % 16 == 0;
+  }
+  const bool addb = p.split == 1 && p.bias;
+  f4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (addb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bq[e] = col + e < p.N ? p.bias[col + e] : 0.0f;
+  }
+#pragma unroll 4
+  for (int j = 0; j < BM / 8; ++j) {
+    const int r = (tid >> 5) + 8 * j;
+    const int64_t row = m0 + r;
+    if (row >= p.M) break;
+    f4 v = *reinterpret_cast<const f4*>(ctile + r * EPI_TP + 4 * c4);
+    if (addb) v += bq;
+    float* dst = dst0 + row * pitch + col;
+    if (vec && col + 4 <= p.N) {
+      if (p.split > 1)
+        *reinterpret_cast<f4*>(dst) = v;
+      else
+        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(dst));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.N) dst[e] = v[e];
+    }
   }
 }
 
