@@ -94,23 +94,30 @@ __device__ __forceinline__ const ST* scale_ptr(const GemvParams& p) {
   else return p.scales;
 }
 
-// sum_k x * c over one 32-k chunk (four packed words), fp32 throughout
+// sum_k x * c over one 32-k chunk (four packed words), fp32 throughout.
+// Each word's eight products are summed in k-pair order into their own
+// partial; the four partials' chains are issued interleaved (word innermost),
+// so consecutive FMAs never depend on each other.
 template <int ORDER>
 __device__ __forceinline__ float chunk_dot(const uint32_t (&q)[4], const float (&x)[32],
                                            const Magic& mg) {
-  float part[4];
+  h2 c[4][4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    h2 c[4];
-    unpack_word(q[d], mg, c);
-    float a = 0.0f;
+  for (int d = 0; d < 4; ++d) unpack_word(q[d], mg, c[d]);
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      a = __builtin_fmaf((float)c[pp].x, x[8 * d + pair_k<ORDER>(pp, 0)], a);
-      a = __builtin_fmaf((float)c[pp].y, x[8 * d + pair_k<ORDER>(pp, 1)], a);
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+    {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        part[d] = __builtin_fmaf((float)(h == 0 ? c[d][pp].x : c[d][pp].y),
+                                 x[8 * d + pair_k<ORDER>(pp, h)], part[d]);
+      // keep the four chains interleaved (the scheduler would otherwise
+      // issue them one after another)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    part[d] = a;
-  }
   return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
