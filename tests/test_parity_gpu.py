@@ -136,6 +136,27 @@ def test_row_pitches_and_unaligned_rows(math):
                pad=(4, 3, 0, 1), label="pitches")
 
 
+# ---- the pipelined GEMM's output stores ----------------------------------
+# The pipelined kernel (dword-aligned weight rows, K % 32 == 0, power-of-two
+# groups >= 32 or per-channel) stores 16-byte row segments when the output
+# rows allow it and element by element otherwise; split-K partials likewise.
+# These shapes hit every branch: an output pitch that is not a multiple of 4,
+# a last column quad that is partly past N, M tails, and split-K partials with
+# N % 4 != 0, each with a bias and guard columns around the output.
+@pytest.mark.parametrize("M,K,N,gs,pad_out", [
+    (200, 512, 203, 32, 3),     # no split; element stores (output pitch 206)
+    (130, 2048, 8202, 64, 2),   # no split; 16-byte stores, last quad ragged, M tail
+    (64, 8192, 130, 128, 0),    # split K; element stores of partials (N % 4 == 2)
+    (96, 4096, 264, 32, 0),     # split K; 16-byte stores of partials
+    (333, 512, 516, 0, 0),      # per-channel scales; 16-byte stores, M tail
+])
+def test_pipelined_gemm_output_stores(M, K, N, gs, pad_out):
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=M + K + N)
+    check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
+               pad=(0, 0, 0, pad_out), label="pipe-stores")
+
+
 # ---- exact special cases (bit-for-bit on every path) ---------------------
 @pytest.mark.parametrize("math,M", [("f32", 1), ("f32", 3), ("f16", 1), ("f16", 70),
                                     ("auto", 200)])
