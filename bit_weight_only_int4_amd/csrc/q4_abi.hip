@@ -41,18 +41,24 @@ bool aligned(const void* p, uintptr_t a) {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
 // Q4_MATH_AUTO: fp32 for M == 1 (the GEMV) and for a few activation rows
-// whose products are few (the low-batch GEMV reads the weights once for all
-// rows and, measured on MI355X, beats the MFMA GEMM there); binary16 MFMA
-// otherwise.  Sizes only, so the workspace query and the call agree.
+// whose products are few (the low-batch GEMV reads the weights once per
+// block of rows and, measured on MI355X, beats the MFMA GEMM there, whose
+// pre-pass, launches and split-K reduce cost 10-25 us at small M); binary16
+// MFMA otherwise.  Measured over the Llama-shaped projections at
+// M = 2 .. 16: the fp32 kernel is faster for every M <= 16 with
+// M * N * K <= 2^26, and at M = 2 up to M * N * K = 2^30 (the lm_head
+// projection); beyond these the GEMM is faster or within 10%.  Sizes only,
+// so the workspace query and the call agree.
 int32_t resolve_math(int32_t math, int64_t M, int64_t N, int64_t K, int64_t group_size) {
   if (math != Q4_MATH_AUTO) return math;
   if (M == 1) return Q4_MATH_F32;
   const bool staged = group_size == 0 || group_size >= K ||
                       ((group_size & (group_size - 1)) == 0 && group_size >= 32 &&
                        group_size <= 2048);
-  if (staged && K % 4 == 0 && M <= q4::gemv_lowbatch_max_rows(K) &&
-      (double)M * (double)N * (double)K <= (double)(1LL << 29))
-    return Q4_MATH_F32;
+  const double mnk = (double)M * (double)N * (double)K;
+  const bool few = (M <= 16 && mnk <= (double)(1LL << 26)) ||
+                   (M <= 2 && mnk <= (double)(1LL << 30));
+  if (staged && K % 4 == 0 && few) return Q4_MATH_F32;
   return Q4_MATH_F16;
 }
 

@@ -106,14 +106,6 @@ static int lowbatch_rows(int64_t M, int waves_k) {
   return mb;
 }
 
-int gemv_lowbatch_max_rows(int64_t K) {
-  const int64_t spans = (K + 2047) / 2048;
-  const int64_t split = (spans + 7) / 8;
-  const int waves_k = (int)((spans + split - 1) / split);
-  const int cap = 8 / waves_k;
-  return cap >= 2 ? cap : 1;
-}
-
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   (void)group_size;
   GemvPlan pl{};

@@ -68,8 +68,6 @@ template <typename ST>
 hipError_t launch_gemv_kernels(const GemvParams& p, const GemvLaunch& l, hipStream_t s);
 // (instantiated for float and _Float16 in q4_gemv_s32.hip / q4_gemv_s16.hip)
 
-// most activation rows one low-batch workgroup holds for this K (1: none)
-int gemv_lowbatch_max_rows(int64_t K);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
 hipError_t launch_gemv(const GemvParams& p, int order, bool qa4, hipStream_t s);
 

@@ -59,10 +59,11 @@ typedef int32_t q4_status;
 #define Q4_ORDER_HIGH_FIRST 1 /* qcs4w packer: byte = (q[even k] << 4) | q[odd k] */
 
 /* Arithmetic of q4_linear. */
-#define Q4_MATH_AUTO 0 /* M == 1: F32 GEMV; small batches (2 <= M <= 8 / ceil(K /
-                          2048), M * N * K <= 2^29, power-of-two groups >= 32 or
-                          per-channel, K % 4 == 0): F32 low-batch GEMV; else
-                          F16 MFMA GEMM.  Decided on sizes alone. */
+#define Q4_MATH_AUTO 0 /* M == 1: F32 GEMV; small batches (M <= 16 with
+                          M * N * K <= 2^26, or M == 2 with M * N * K <= 2^30;
+                          power-of-two groups >= 32 or per-channel, K % 4 == 0):
+                          F32 low-batch GEMV; else F16 MFMA GEMM.  Decided on
+                          sizes alone. */
 #define Q4_MATH_F32 1  /* pure fp32: f32 dequant, f32 products, f32 sums */
 #define Q4_MATH_F16 2  /* binary16 operands (x and dequantized w) on MFMA,
                           fp32 accumulation; never binary16 accumulation */
