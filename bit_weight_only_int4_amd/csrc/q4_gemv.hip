@@ -117,15 +117,20 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   // Rows per wave and row groups per workgroup, from a sweep on MI355X over
   // the Llama-shaped projections: about four waves per workgroup, four rows
   // per wave unless that leaves fewer than 2048 waves (then two), eight
-  // only for deep K (more than four spans) where eight still give 2048.
+  // only for deep K (more than four spans) where eight still give 2048;
+  // for one activation row, two spans over at most 4096 rows run two rows
+  // per wave in four row groups, and four spans two row groups (eight waves
+  // sharing the activations).
   pl.mb = lowbatch_rows(M, pl.waves_k);
   const int64_t mrows = (M + pl.mb - 1) / pl.mb;  // activation row blocks
   auto waves = [&](int r) { return ((N + r - 1) / r) * pl.waves_k * pl.split * mrows; };
   int rows = 4;
   if (waves(4) < 2048) rows = 2;
   if (pl.waves_k > 4 && waves(8) >= 2048) rows = 8;
-  pl.rows_per_wave = rows;
   int wr = 4 / pl.waves_k;
+  if (pl.mb == 1 && mrows == 1 && pl.waves_k == 2 && N <= 4096) { rows = 2; wr = 4; }
+  if (pl.mb == 1 && mrows == 1 && pl.waves_k == 4) wr = 2;
+  pl.rows_per_wave = rows;
   if (wr < 1) wr = 1;
   while (wr > 1 && (int64_t)(wr / 2) * rows >= N) wr /= 2;
   pl.waves_r = wr;
