@@ -103,6 +103,30 @@ def test_workspace_is_required_when_the_plan_splits():
     assert call(a)[0] == ALIAS
 
 
+# (M, K, N, group_size, runs an fp32 GEMV): the automatic choice at and
+# around the boundaries of its rule (M <= 16 with M*N*K <= 2^26, or M == 2
+# with M*N*K <= 2^30; staged or per-channel scales; K % 4 == 0)
+REGIME = [
+    (1, 2048, 128257, 0, True), (1, 14336, 4096, 128, True),
+    (4, 2048, 8192, 32, True), (4, 2048, 8193, 32, False),
+    (16, 2048, 2048, 32, True), (16, 2048, 2049, 32, False), (17, 256, 64, 32, False),
+    (2, 2048, 262144, 0, True), (2, 2048, 262145, 0, False), (3, 2048, 128257, 0, False),
+    (4, 2048, 300, 8, False), (4, 2046, 300, 0, False), (4, 2048, 300, 48, False),
+]
+
+
+@pytest.mark.parametrize("M,K,N,gs,gemv", REGIME)
+def test_automatic_regime_from_sizes(M, K, N, gs, gemv):
+    """The automatic choice depends on sizes alone.  Below 16384 k the fp32
+    kernels need no workspace while the MFMA GEMM always does (its binary16
+    activations), so the workspace query shows which one a call runs; an
+    explicit math overrides the choice."""
+    L = b.lib()
+    assert (L.q4_linear_workspace_bytes(M, N, K, gs, 0) == 0) == gemv
+    assert L.q4_linear_workspace_bytes(M, N, K, gs, 1) == 0
+    assert L.q4_linear_workspace_bytes(M, N, K, gs, 2) > 0
+
+
 def test_workspace_query_is_zero_for_invalid_sizes():
     L = b.lib()
     assert L.q4_linear_workspace_bytes(-1, 10, 10, 0, 0) == 0
