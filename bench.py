@@ -250,7 +250,10 @@ def launch_times(suite, torch, reps=64):
     rows = []
     for i, it in enumerate(suite.items):
         g = suite.kernel_graph(i, reps)
-        time_graph(torch, g, 1)
+        # untimed replays first: the first few milliseconds of a fresh graph
+        # on a given set of buffers run measurably slower (up to 15% for the
+        # MFMA kernels)
+        time_graph(torch, g, 3)
         rows.append(time_graph(torch, g, 4) / (4 * reps))
     return rows
 
@@ -475,7 +478,8 @@ def main():
     if args.only in ("prefill", "both"):
         print(f"[bench] prefill M={args.prefill_m}", file=sys.stderr, flush=True)
         pre = Suite(pre_projs, torch, b, make_inputs)
-        m = measure(pre, max(8, args.steps // 8), max(4, args.warmup // 8), torch)
+        # at least two untimed passes over the rotating copies
+        m = measure(pre, max(8, args.steps // 8), max(2 * pre.copies, args.warmup // 8), torch)
         times = launch_times(pre, torch, reps=16)
         # one layer call is the binary16 pre-pass plus the MFMA GEMM (plus the
         # split-K reduce where the plan splits K); timed together per call
