@@ -110,11 +110,13 @@ class Suite:
         torch.cuda.synchronize()
         return g
 
-    def step_graph(self):
+    def step_graph(self, nsteps):
+        """A graph of exactly nsteps steps; step s uses weight copy s % copies,
+        so consecutive steps stream different copies from HBM."""
         def body():
-            for c in range(self.copies):
+            for st in range(nsteps):
                 for i in range(len(self.items)):
-                    self.launch(i, c)
+                    self.launch(i, st % self.copies)
         return self.capture(body)
 
     def kernel_graph(self, i, reps):
@@ -232,15 +234,16 @@ def time_graph(torch, g, replays):
 
 
 def measure(suite, steps, warmup, torch):
-    g = suite.step_graph()
-    per_graph = suite.copies
-    replays = max(1, -(-steps // per_graph))
-    wreps = max(1, -(-warmup // per_graph))
-    time_graph(torch, g, wreps)
-    secs = time_graph(torch, g, replays)
-    nsteps = replays * per_graph
-    return dict(steps=nsteps, warmup=wreps * per_graph, seconds=secs,
-                ms_per_step=secs / nsteps * 1e3)
+    """Exactly `warmup` untimed steps, then exactly `steps` timed steps, each
+    as one graph replay bracketed by device synchronisation."""
+    steps = max(1, steps)
+    if warmup > 0:
+        gw = suite.step_graph(warmup)
+        time_graph(torch, gw, 1)
+        del gw
+    g = suite.step_graph(steps)
+    secs = time_graph(torch, g, 1)
+    return dict(steps=steps, warmup=warmup, seconds=secs, ms_per_step=secs / steps * 1e3)
 
 
 def launch_times(suite, torch, reps=64):
