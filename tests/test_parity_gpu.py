@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+from bit_weight_only_int4_amd import q4linear as b
 from bit_weight_only_int4_amd.workloads import CONFIGS, make_inputs, small_projection
 from tests.gpu_util import check_case, need_gpu, run_gpu, oracle_full, normalised_error
 from tests.packing import pack
@@ -158,6 +159,36 @@ def test_pipelined_gemm_output_stores(M, K, N, gs, pad_out):
     x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=M + K + N)
     check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
                pad=(0, 0, 0, pad_out), label="pipe-stores")
+
+
+@pytest.mark.parametrize("math,M,K,N", [
+    ("f16", 130, 2048, 1030),   # pipelined GEMM, no split: the output's own stores
+    ("f16", 64, 8192, 260),     # pipelined GEMM, split K: the reduce kernel's stores
+    ("f16", 70, 1002, 300),     # general GEMM
+    ("f32", 1, 2048, 515),      # GEMV
+    ("f32", 4, 2048, 515),      # low-batch GEMV
+])
+def test_output_not_16_byte_aligned(math, M, K, N):
+    """out may start at any 4-byte boundary: a view that begins one float
+    into its buffer (so no 16-byte vector store is legal) gets the same
+    values, and nothing outside [M, N] is written."""
+    need_gpu()
+    dev = torch.device("cuda")
+    x, qw, s, bias = inputs(M, K, N, 32, bias=True, seed=M + N)
+    obuf = torch.full((M + 2, N + 5), float("nan"), dtype=torch.float32, device=dev)
+    out = obuf[:M, 1:N + 1]
+    assert out.data_ptr() % 16 != 0
+    b.linear(x.to(dev), qw.to(dev), s.to(dev), bias.to(dev), K=K, group_size=32, math=math,
+             out=out)
+    torch.cuda.synchronize()
+    full = obuf.cpu().numpy()
+    assert np.all(np.isnan(full[:, 0])) and np.all(np.isnan(full[:, N + 1:]))
+    assert np.all(np.isnan(full[M:, :]))
+    got = full[:M, 1:N + 1]
+    ref, den = oracle_full(x, qw, s, bias, K=K, gs=32, order="low_first")
+    err = normalised_error(got, ref, den)
+    assert not np.any(np.isnan(got))
+    assert err <= (2e-3 if math == "f16" else 1e-5), err
 
 
 # ---- exact special cases (bit-for-bit on every path) ---------------------
