@@ -295,3 +295,33 @@ def test_backward_f16_full_size_sampled(name):
         err = normalised_error(got.cpu().numpy()[ms, ks], ref, den)
         log(f"          max normalised error={err:.3e}")
         assert err <= BWD_TOL["bwd_f16"]
+
+
+@pytest.mark.parametrize("math,M,N,K", [
+    ("f16", 130, 600, 1032),   # MFMA gradient, no split over N
+    ("f16", 64, 4096, 264),    # MFMA gradient, split over N (the reduce kernel's stores)
+    ("f32", 3, 700, 1000),     # fp32 gradient
+])
+def test_backward_dx_not_16_byte_aligned(math, M, N, K):
+    """d_x may start at any 4-byte boundary: a view one float into its
+    buffer gets the same values and nothing outside [M, K] is written."""
+    need_gpu()
+    dev = torch.device("cuda")
+    g = torch.Generator().manual_seed(M + N + K)
+    dout = torch.randn(M, N, generator=g)
+    qw = torch.randint(0, 256, (N, (K + 1) // 2), dtype=torch.uint8, generator=g)
+    s = 0.005 + 0.015 * torch.rand(-(-K // 32), N, generator=g)
+    buf = torch.full((M + 2, K + 5), float("nan"), dtype=torch.float32, device=dev)
+    dx = buf[:M, 1:K + 1]
+    assert dx.data_ptr() % 16 != 0
+    b.linear_backward(dout.to(dev), qw.to(dev), s.to(dev), K=K, group_size=32, math=math, dx=dx)
+    torch.cuda.synchronize()
+    full = buf.cpu().numpy()
+    assert np.all(np.isnan(full[:, 0])) and np.all(np.isnan(full[:, K + 1:]))
+    assert np.all(np.isnan(full[M:, :]))
+    got = full[:M, 1:K + 1]
+    ref, den = orc.linear_backward(dout.numpy(), qw.numpy(), s.numpy(), K=K, group_size=32)
+    assert not np.any(np.isnan(got))
+    err = normalised_error(got, ref, den)
+    log(f"[case] dx unaligned {math} M={M} N={N} K={K}: max normalised error {err:.3e}")
+    assert err <= (2e-3 if math == "f16" else 1e-5), err
