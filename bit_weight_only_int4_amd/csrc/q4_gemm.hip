@@ -583,9 +583,10 @@ gemm_pipe_kernel(const GemmParams p) {
   // the ring is free: the tile goes through LDS and leaves as 16-byte
   // row-contiguous stores (a wave writes two 512-byte row segments per
   // store), non-temporal for the output, which nothing here reads again.
-  // The output write is the one serial phase after the MFMA loop; 4-byte
-  // stores straight from the MFMA layout (two 128-byte segments per store)
-  // measured about 1.5x slower at M = 512.
+  // The output write is the one serial phase after the MFMA loop: with
+  // 4-byte stores straight from the MFMA layout (two 128-byte segments per
+  // store) it took about 7.5 us of a 34 us call at M = 512, N = 8192; staged
+  // like this, about 1.6 us.
   // Lane l, element v of a 32x32 block holds row 8*(v/4) + 4*(l/32) + v%4
   // and column l%32; the row pitch (EPI_TP floats) puts the two row halves
   // of one LDS store on disjoint banks.
