@@ -463,17 +463,19 @@ gemv_lb_kernel(const GemvParams p) {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float part[4];
+      // each word's products in k-pair order into its own partial, the four
+      // chains issued interleaved (as in chunk_dot)
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        float a = 0.0f;
+      for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          a = __builtin_fmaf((float)c[r][d][pp].x, xr[8 * d + pair_k<ORDER>(pp, 0)], a);
-          a = __builtin_fmaf((float)c[r][d][pp].y, xr[8 * d + pair_k<ORDER>(pp, 1)], a);
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            part[d] = __builtin_fmaf((float)(h == 0 ? c[r][d][pp].x : c[r][d][pp].y),
+                                     xr[8 * d + pair_k<ORDER>(pp, h)], part[d]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        part[d] = a;
-      }
       const float dot = (part[0] + part[1]) + (part[2] + part[3]);
       acc[m][r] = SMODE == kStaged ? sv[r] * dot : dot;
     }
