@@ -323,6 +323,19 @@ def copy_calibration(torch, mib=1024, reps=8):
                 us=round(secs * 1e6, 2), gbs_read_plus_write=round(2 * n * 4 / secs / 1e9, 1))
 
 
+def gpu_clocks():
+    """Current shader and memory clocks of GPU 0 as rocm-smi reports them
+    (read in a child process; context for the timings), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        return {k.split()[0]: v.strip("()") for k, v in card.items() if "clock speed" in k}
+    except Exception:
+        return None
+
+
 def cpu_baseline(projs, budget_s, unit):
     """The oracle, as is, over a bounded sample of the step: a slice of the
     output columns of every projection (whole K, all M rows), repeated until
@@ -391,6 +404,7 @@ def main():
     b.lib()  # fail loudly if the HIP library is missing
 
     result = {}
+    clocks_before = gpu_clocks()
     if args.copy_calibration:
         result["copy"] = copy_calibration(torch)
         print(f"[bench] copy: {result['copy']}", file=sys.stderr, flush=True)
@@ -496,6 +510,7 @@ def main():
                           unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4),
                           traffic=None, kernel="gemm_f16 call (pre-pass + GEMM)",
                           avg_launch_us=round(t_sum / len(times) * 1e6, 3)))
+        result["clocks_after_prefill"] = gpu_clocks()
         print(f"[bench] prefill done: {m['ms_per_step']:.4f} ms/step", file=sys.stderr,
               flush=True)
         del pre
@@ -564,6 +579,8 @@ def main():
             r = result[kind]
             line[kind] = dict(r, config={"workload": f"decode_1b projections: {what}"})
     line["cpu_baseline"] = cpu
+    line["gpu_clocks"] = {"before": clocks_before,
+                          "after_prefill": result.get("clocks_after_prefill")}
     if "copy" in result:
         line["copy_calibration"] = result["copy"]
     print(json.dumps(line), flush=True)
