@@ -51,7 +51,7 @@ typedef int32_t q4_status;
                                  below row width, unknown enum value */
 #define Q4_ERR_ALIAS 2        /* out overlaps an input */
 #define Q4_ERR_WORKSPACE 3    /* workspace NULL or smaller than required */
-#define Q4_ERR_UNSUPPORTED 4  /* a valid request this build does not run */
+#define Q4_ERR_UNSUPPORTED 4  /* a valid request the library does not implement */
 #define Q4_ERR_DEVICE 5       /* the HIP runtime reported a launch error */
 
 /* Nibble order of the packed bytes (page 5, Constraints (2)). */
