@@ -18,6 +18,15 @@ seeded with ``seed``, in the order x -> packed bytes -> scales -> bias):
 The shapes are those of the Llama-3.2-1B and Llama-3.1-8B projections that
 the pages measure (page 4, "Kernel level"; page 1, the steel and pwdq
 entries), drawn synthetically: no model weights are used.
+
+Pages cited by number (the texts this layer is written from):
+  page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"
+          (its stack entries #20730 ... #20801);
+  page 2: ExecuTorch PR #20847, "[WebGPU] Add optimized linear_fp32 op";
+  page 3: ExecuTorch PR #21070, "Add fp32 matmul ops (mm, bmm, linear)"
+          (its stack entries #20917 ... #21005);
+  page 4: Apache TVM PR #20425, the dlight GEMV rule's webgpu branch;
+  page 5: ExecuTorch PR #21211, "[WebGPU] Add linear_qcs4w op".
 """
 from dataclasses import dataclass, replace
 from typing import Optional, Tuple

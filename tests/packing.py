@@ -5,6 +5,15 @@ Constraints (2)), not from any unpacker:
   * q4gsw packer ("low_first"):  byte = (code[odd k] << 4) | code[even k]
   * qcs4w packer ("high_first"): byte = (code[even k] << 4) | code[odd k]
 For an odd K the last byte's unused nibble is ``pad`` (0..15).
+
+Pages cited by number (the texts this layer is written from):
+  page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"
+          (its stack entries #20730 ... #20801);
+  page 2: ExecuTorch PR #20847, "[WebGPU] Add optimized linear_fp32 op";
+  page 3: ExecuTorch PR #21070, "Add fp32 matmul ops (mm, bmm, linear)"
+          (its stack entries #20917 ... #21005);
+  page 4: Apache TVM PR #20425, the dlight GEMV rule's webgpu branch;
+  page 5: ExecuTorch PR #21211, "[WebGPU] Add linear_qcs4w op".
 """
 import numpy as np
 

@@ -5,6 +5,15 @@ Each test names what it pins; together they are chosen so that a plausible
 mistake in the oracle (swapped nibbles, a wrong signed offset, a transposed
 scale index, a dropped bias, a K-tail that reads the pad nibble) fails at
 least one of them.
+
+Pages cited by number (the texts this layer is written from):
+  page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"
+          (its stack entries #20730 ... #20801);
+  page 2: ExecuTorch PR #20847, "[WebGPU] Add optimized linear_fp32 op";
+  page 3: ExecuTorch PR #21070, "Add fp32 matmul ops (mm, bmm, linear)"
+          (its stack entries #20917 ... #21005);
+  page 4: Apache TVM PR #20425, the dlight GEMV rule's webgpu branch;
+  page 5: ExecuTorch PR #21211, "[WebGPU] Add linear_qcs4w op".
 """
 import json
 import os

@@ -16,6 +16,15 @@ and by the test-side packer written from the pages' packers.
 Binary16 scales (page 4's q4f16_1 weights, read as 4-bit codes with
 binary16 group scales): every one of the 65536 bit patterns widens to numpy's
 binary16 value, and a worked example computed by hand.
+
+Pages cited by number (the texts this layer is written from):
+  page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"
+          (its stack entries #20730 ... #20801);
+  page 2: ExecuTorch PR #20847, "[WebGPU] Add optimized linear_fp32 op";
+  page 3: ExecuTorch PR #21070, "Add fp32 matmul ops (mm, bmm, linear)"
+          (its stack entries #20917 ... #21005);
+  page 4: Apache TVM PR #20425, the dlight GEMV rule's webgpu branch;
+  page 5: ExecuTorch PR #21211, "[WebGPU] Add linear_qcs4w op".
 """
 import json
 import os

@@ -5,6 +5,15 @@ tiles plus ragged tails), through the C ABI.
 Shapes include the pages' own test shapes (page 1: steel M=96 K=2048 N=256,
 steel_f16_edge M=70 K=1024 N=136, pwdq gs 64 and gs 8, the deep-K
 128 x 8192 x 2048 case) and the decode GEMV of page 4 at reduced N.
+
+Pages cited by number (the texts this layer is written from):
+  page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"
+          (its stack entries #20730 ... #20801);
+  page 2: ExecuTorch PR #20847, "[WebGPU] Add optimized linear_fp32 op";
+  page 3: ExecuTorch PR #21070, "Add fp32 matmul ops (mm, bmm, linear)"
+          (its stack entries #20917 ... #21005);
+  page 4: Apache TVM PR #20425, the dlight GEMV rule's webgpu branch;
+  page 5: ExecuTorch PR #21211, "[WebGPU] Add linear_qcs4w op".
 """
 import numpy as np
 import pytest
