@@ -16,7 +16,12 @@
 //    order described below, zero-padded to whole tiles, into the workspace;
 //    the GEMM then reads 2 bytes per activation instead of 4 on every
 //    column tile that reuses it, and needs no row or K masks for them.
-//  * Workgroups own 128 x 128 output tiles; K advances 64 per step.
+//  * Workgroups own 128 x 128 output tiles; K advances 64 per step.  The
+//    pipelined kernel widens them to 128 x 256 where 128 x 128 tiles would
+//    need more than one round of the 256 CUs and no split-K is planned:
+//    each wave then owns 128 x 64 outputs, which halves the activation LDS
+//    reads per MFMA (measured 9-11% faster on such shapes, slower where the
+//    wider tiles leave CUs idle).
 //  * Inside every 8-element group the k order follows the nibble order of
 //    the packed word (pairs (i, i+4)); the activations are stored with the
 //    same permutation, so A and B fragments pair up k for k.
@@ -359,8 +364,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // bytes, and with 32-wide groups lane half lb lies in group 2*step + lb.
 //
 // LDS per stage: activations 128 rows x 8 chunks of 16 bytes, XOR-swizzled
-// (a_slot); packed weights [128 columns][32 bytes]; scales
-// [4 waves][2 halves][32 columns] floats.
+// (a_slot); packed weights [128 NI columns][32 bytes]; scales
+// [4 waves][NI blocks][2 halves][32 columns] floats.  Five stages: 105 KiB
+// with NI = 1, 130 KiB with NI = 2.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -369,17 +375,20 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // in order, and an MFMA keeps the matrix unit busy for 32 cycles, so each
 // MFMA is followed by the next step's loads and LDS reads and by a few
 // dequant VALU ops, which issue while it runs.
-template <int K>
+// NI: 32-column blocks per wave (16 NI MFMAs, 4 + 2 NI buffer loads and
+// 1 + 16 + 2 NI LDS reads per step and wave).
+template <int K, int NI>
 __device__ __forceinline__ void interleave_slots() {
-  if constexpr (K < 16) {
+  if constexpr (K < 16 * NI) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if constexpr (K < 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
-    if constexpr (K < 9) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+    if constexpr (K < 4 + 2 * NI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
+    if constexpr (K < 7 + 2 * NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
     if constexpr (K >= 4) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-    interleave_slots<K + 1>();
+    interleave_slots<K + 1, NI>();
   }
 }
-__device__ __forceinline__ void interleave_step() { interleave_slots<0>(); }
+template <int NI>
+__device__ __forceinline__ void interleave_step() { interleave_slots<0, NI>(); }
 
 // A wave-uniform pointer placed in scalar registers (a buffer resource must
 // live in SGPRs; an address computed with 64-bit vector arithmetic would
@@ -400,7 +409,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-constexpr int PIPE_BN = 128;
 constexpr int PIPE_NT = 256;
 
 // LDS slot (16 bytes) of activation chunk c (0..7) of tile row r.  Rows are
@@ -411,29 +419,37 @@ __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ ((r >>
 // row pitch, in floats, of the output tile the epilogue stages in LDS
 constexpr int EPI_TP = 136;
 
-template <int NSTAGE>
+template <int NSTAGE, int NI>
 struct PipeSmem {
-  uint32_t a[NSTAGE][BM * KS / 2];       // binary16 activations, swizzled
-  uint32_t q[NSTAGE][PIPE_BN * KS / 8];  // packed weights, 32 bytes per column
-  float s[NSTAGE][PIPE_NT];              // scales (grouped only)
+  uint32_t a[NSTAGE][BM * KS / 2];          // binary16 activations, swizzled
+  uint32_t q[NSTAGE][128 * NI * KS / 8];    // packed weights, 32 bytes per column
+  float s[NSTAGE][PIPE_NT * NI];            // scales (grouped only)
 };
 
 // S16: binary16 scales (q4f16_1).  A lane's scale DMA then fetches the
 // dword that holds its column's scale and its even/odd neighbour's (N and
 // lds even, scales 4-byte aligned: no dword straddles the array's end) and
 // keeps the half of its own column parity.
-template <int ORDER, bool PERCH, int NSTAGE, bool S16>
+//
+// NI: 32-column blocks per wave.  NI = 1: 128 x 128 tiles, a wave owns
+// 128 x 32 outputs.  NI = 2: 128 x 256 tiles, a wave owns 128 x 64 (two
+// column blocks sharing each activation fragment), which halves the
+// activation LDS reads per MFMA; the per-output k order is the same.
+template <int ORDER, bool PERCH, int NSTAGE, bool S16, int NI>
 __global__ void __launch_bounds__(PIPE_NT)
 gemm_pipe_kernel(const GemmParams p) {
   static_assert(NSTAGE >= 3 && NSTAGE <= 6, "pipeline depth");
-  static_assert(6 * (NSTAGE - 1) < 64, "vmcnt range");
-  static_assert(sizeof(PipeSmem<NSTAGE>) >= BM * EPI_TP * sizeof(float),
+  static_assert(NI == 1 || NI == 2, "column blocks per wave");
+  constexpr int PER_STAGE = PERCH ? 4 + NI : 4 + 2 * NI;  // buffer loads per stage per lane
+  static_assert(PER_STAGE * (NSTAGE - 1) < 64, "vmcnt range");
+  static_assert(sizeof(PipeSmem<NSTAGE, NI>) >= BM * EPI_TP * sizeof(float),
                 "the epilogue stages the output tile in the pipeline's LDS");
+  static_assert(sizeof(PipeSmem<NSTAGE, NI>) <= 160 * 1024, "LDS per workgroup");
   // The kernel's only LDS object: with a second one the compiler can no
   // longer tell the loop's LDS reads from the LDS-DMA writes in flight and
   // waits for all of them (vmcnt(0)) before every step's reads, which drains
   // the ring (measured 35% slower).
-  __shared__ __attribute__((aligned(16))) PipeSmem<NSTAGE> sm;
+  __shared__ __attribute__((aligned(16))) PipeSmem<NSTAGE, NI> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -445,7 +461,8 @@ gemm_pipe_kernel(const GemmParams p) {
   const int tm = (int)(tile % (uint32_t)p.tiles_m);
   const int tn = (int)(tile / (uint32_t)p.tiles_m);
   const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * PIPE_BN;
+  const int64_t n0 = (int64_t)tn * (128 * NI);
+  const int c0 = 32 * NI * w;  // first tile column of this wave
   const int z = blockIdx.z;
   const int kz0 = (int)((int64_t)z * p.k_per_split);
   const int kz1 = (int)((kz0 + p.k_per_split < p.K) ? kz0 + p.k_per_split : p.K);
@@ -471,10 +488,15 @@ gemm_pipe_kernel(const GemmParams p) {
     const int row = j >> 3, c = (j & 7) ^ ((row >> 1) & 7);
     va[u] = (uint32_t)((row * p.x16_pitch + 8 * c) * 2);
   }
-  // packed weights: lane -> column 32w + lane/2, 16-byte half lane & 1
-  const uint32_t vq = (uint32_t)((n0 + 32 * w + (lane >> 1)) * p.ldq + 16 * (lane & 1));
-  // scales: lane -> half lb's group, column 32w + li
-  const uint32_t vs = (uint32_t)(((n0 + 32 * w + li) & (S16 ? ~1 : ~0)) * SB);
+  // packed weights of column block u: lane -> column c0 + 32u + lane/2,
+  // 16-byte half lane & 1
+  uint32_t vq[2], vs[2];  // fixed bound: a lambda capturing a template-sized array loses its host stub
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    vq[u] = (uint32_t)((n0 + c0 + 32 * u + (lane >> 1)) * p.ldq + 16 * (lane & 1));
+    // scales of block u: lane -> half lb's group, column c0 + 32u + li
+    vs[u] = (uint32_t)(((n0 + c0 + 32 * u + li) & (S16 ? ~1 : ~0)) * SB);
+  }
   const uint32_t lds4 = (uint32_t)(p.lds * SB);
   const int l2g = p.log2_gs;
 
@@ -484,43 +506,56 @@ gemm_pipe_kernel(const GemmParams p) {
     for (int u = 0; u < 4; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_ptr_t)((char*)&sm.a[st][0] + (w * 4 + u) * 1024), 16, va[u] + 2 * kb, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rq, (lds_ptr_t)((char*)&sm.q[st][0] + w * 1024), 16, vq + (kb >> 1), 0, 0, 0);
-    if (!PERCH)
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_ptr_t)((char*)&sm.s[st][0] + w * 256), 4,
-          vs + ((kb + 32 * lb) >> l2g) * lds4, 0, 0, 0);
+          rq, (lds_ptr_t)((char*)&sm.q[st][0] + (w * NI + u) * 1024), 16, vq[u] + (kb >> 1), 0, 0, 0);
+    if (!PERCH)
+#pragma unroll
+      for (int u = 0; u < NI; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_ptr_t)((char*)&sm.s[st][0] + (w * NI + u) * 256), 4,
+            vs[u] + ((kb + 32 * lb) >> l2g) * lds4, 0, 0, 0);
   };
-  constexpr int PER_STAGE = PERCH ? 5 : 6;  // buffer loads per stage per lane
 
-  h2 s16c = {(_Float16)0.0f, (_Float16)0.0f};
-  if (PERCH) {
-    const int64_t col = n0 + 32 * w + li;
-    s16c = splat_f16(col < p.N ? scale_at(p.scales, p.scales16, col) : 0.0f);
+  h2 s16c[2];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    s16c[u] = h2{(_Float16)0.0f, (_Float16)0.0f};
+    if (PERCH) {
+      const int64_t col = n0 + c0 + 32 * u + li;
+      s16c[u] = splat_f16(col < p.N ? scale_at(p.scales, p.scales16, col) : 0.0f);
+    }
   }
   const Magic mg = Magic::make();
 
-  f16v acc[4];
+  f16v acc[NI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int u = 0; u < NI; ++u)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[u][i][v] = 0.0f;
 
   // A step's operands, read from LDS into registers one step ahead, and its
   // weights dequantized one step ahead: while the MFMAs of step s run, the
   // wave issues the LDS reads of step s + 1 and unpacks its weights.
   struct Frag {
-    h8 a[4][4];  // [t][i]: activation rows 32i + li, chunk 4 lb + t
-    h8 b[4];     // [t]: binary16 weights of this lane's column, chunk 4 lb + t
-    u32x4 q;     // packed words of this lane's column, chunks 4 lb .. 4 lb + 3
-    float s;     // scale of this lane's half-step (grouped)
+    h8 a[4][4];   // [t][i]: activation rows 32i + li, chunk 4 lb + t
+    h8 b[NI][4];  // [u][t]: binary16 weights of this lane's column in block u, chunk 4 lb + t
+    u32x4 q[NI];  // packed words of those columns, chunks 4 lb .. 4 lb + 3
+    float s[NI];  // their scales for this lane's half-step (grouped)
   };
   auto read_frag = [&](int st, Frag& f) {
-    f.q = *reinterpret_cast<const u32x4*>((const char*)&sm.q[st][0] + w * 1024 + li * 32 + lb * 16);
-    if (!PERCH && !S16) f.s = sm.s[st][w * 64 + lane];
-    if (!PERCH && S16) {
-      const uint32_t d = __builtin_bit_cast(uint32_t, sm.s[st][w * 64 + lane]);
-      f.s = (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> (16 * (li & 1))));
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      f.q[u] = *reinterpret_cast<const u32x4*>((const char*)&sm.q[st][0] + (w * NI + u) * 1024 +
+                                               li * 32 + lb * 16);
+      if (!PERCH && !S16) f.s[u] = sm.s[st][(w * NI + u) * 64 + lane];
+      if (!PERCH && S16) {
+        const uint32_t d = __builtin_bit_cast(uint32_t, sm.s[st][(w * NI + u) * 64 + lane]);
+        f.s[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> (16 * (li & 1))));
+      }
     }
     const char* abase = (const char*)&sm.a[st][0];
 #pragma unroll
@@ -530,24 +565,29 @@ gemm_pipe_kernel(const GemmParams p) {
         f.a[t][i] = *reinterpret_cast<const h8*>(abase + a_slot(i * 32 + li, 4 * lb + t) * 16);
   };
   auto dequant = [&](Frag& f) {
-    const h2 s16 = PERCH ? s16c : splat_f16(f.s);
-    const uint32_t qw4[4] = {f.q.x, f.q.y, f.q.z, f.q.w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      h2 c[4];
-      unpack_word(qw4[t], mg, c);
-      h2 d[4];
+    for (int u = 0; u < NI; ++u) {
+      const h2 s16 = PERCH ? s16c[u] : splat_f16(f.s[u]);
+      const uint32_t qw4[4] = {f.q[u].x, f.q[u].y, f.q[u].z, f.q[u].w};
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) d[pp] = dequant_pair_f16(c[pp], s16);
-      f.b[t] = h8{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
+      for (int t = 0; t < 4; ++t) {
+        h2 c[4];
+        unpack_word(qw4[t], mg, c);
+        h2 d[4];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) d[pp] = dequant_pair_f16(c[pp], s16);
+        f.b[u][t] = h8{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
+      }
     }
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[t][i], f.b[t], acc[i], 0, 0, 0);
+      for (int u = 0; u < NI; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[u][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[t][i], f.b[u][t], acc[u][i], 0, 0, 0);
   };
 
   // Pipeline.  The prologue puts steps 0 .. NSTAGE-1 in flight (one per
@@ -582,7 +622,7 @@ gemm_pipe_kernel(const GemmParams p) {
         read_frag((j + 1) % NSTAGE, nxt);
         mma(cur);
         dequant(nxt);
-        interleave_step();
+        interleave_step<NI>();
       }
     }
   }
@@ -590,26 +630,17 @@ gemm_pipe_kernel(const GemmParams p) {
 
   // Epilogue.  Every wave's loads have landed and its LDS reads are done, so
   // the ring is free: the tile goes through LDS and leaves as 16-byte
-  // row-contiguous stores (a wave writes two 512-byte row segments per
-  // store), non-temporal for the output, which nothing here reads again.
+  // row-contiguous stores (with NI = 1 a wave writes two 512-byte row
+  // segments per store; with NI = 2, eight 128-byte ones), non-temporal for
+  // the output, which nothing here reads again.
   // The output write is the one serial phase after the MFMA loop: with
   // 4-byte stores straight from the MFMA layout (two 128-byte segments per
   // store) it took about 7.5 us of a 34 us call at M = 512, N = 8192; staged
   // like this, about 1.6 us.
   // Lane l, element v of a 32x32 block holds row 8*(v/4) + 4*(l/32) + v%4
   // and column l%32; the row pitch (EPI_TP floats) puts the two row halves
-  // of one LDS store on disjoint banks.
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  float* ctile = reinterpret_cast<float*>(&sm);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      ctile[(i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3)) * EPI_TP + 32 * w + li] = acc[i][v];
-  __syncthreads();
-  const int c4 = tid & 31;  // column quad of the tile
-  const int64_t col = n0 + 4 * c4;
+  // of one LDS store on disjoint banks.  With NI = 2 the tile leaves in two
+  // passes, column block h of every wave in pass h.
   float* dst0;
   int64_t pitch;
   bool vec;
@@ -623,47 +654,75 @@ gemm_pipe_kernel(const GemmParams p) {
     vec = p.ldo % 4 == 0 && reinterpret_cast<uintptr_t>(p.out) % 16 == 0;
   }
   const bool addb = p.split == 1 && p.bias;
-  f4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (addb) {
+  float* ctile = reinterpret_cast<float*>(&sm);
+  const int c4 = tid & 31;  // column quad of the staged 128 columns
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bq[e] = col + e < p.N ? p.bias[col + e] : 0.0f;
-  }
+  for (int h = 0; h < NI; ++h) {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        ctile[(i * 32 + 8 * (v >> 2) + 4 * lb + (v & 3)) * EPI_TP + 32 * w + li] = acc[h][i][v];
+    __syncthreads();
+    // staged column 4 c4 is column 4 (c4 % 8) of block h of wave c4 / 8
+    const int64_t col = n0 + 32 * NI * (c4 >> 3) + 32 * h + 4 * (c4 & 7);
+    f4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (addb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bq[e] = col + e < p.N ? p.bias[col + e] : 0.0f;
+    }
 #pragma unroll 4
-  for (int j = 0; j < BM / 8; ++j) {
-    const int r = (tid >> 5) + 8 * j;
-    const int64_t row = m0 + r;
-    if (row >= p.M) break;
-    f4 v = *reinterpret_cast<const f4*>(ctile + r * EPI_TP + 4 * c4);
-    if (addb) v += bq;
-    float* dst = dst0 + row * pitch + col;
-    if (vec && col + 4 <= p.N) {
-      if (p.split > 1)
-        *reinterpret_cast<f4*>(dst) = v;
-      else
-        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(dst));
-    } else {
+    for (int j = 0; j < BM / 8; ++j) {
+      const int r = (tid >> 5) + 8 * j;
+      const int64_t row = m0 + r;
+      if (row >= p.M) break;
+      f4 v = *reinterpret_cast<const f4*>(ctile + r * EPI_TP + 4 * c4);
+      if (addb) v += bq;
+      float* dst = dst0 + row * pitch + col;
+      if (vec && col + 4 <= p.N) {
+        if (p.split > 1)
+          *reinterpret_cast<f4*>(dst) = v;
+        else
+          __builtin_nontemporal_store(v, reinterpret_cast<f4*>(dst));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < p.N) dst[e] = v[e];
+        for (int e = 0; e < 4; ++e)
+          if (col + e < p.N) dst[e] = v[e];
+      }
     }
   }
 }
 
 template <int ORDER, bool PERCH, bool S16>
-hipError_t launch_pipe_t(const GemmParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_pipe_kernel<ORDER, PERCH, 5, S16>), grid, dim3(PIPE_NT), 0, s, p);
+hipError_t launch_pipe_t(const GemmParams& p, dim3 grid, bool wide, hipStream_t s) {
+  if (wide)
+    hipLaunchKernelGGL((gemm_pipe_kernel<ORDER, PERCH, 5, S16, 2>), grid, dim3(PIPE_NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_pipe_kernel<ORDER, PERCH, 5, S16, 1>), grid, dim3(PIPE_NT), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_pipe(const GemmParams& p, dim3 grid, int order, bool perch, hipStream_t s) {
+hipError_t launch_pipe(const GemmParams& p, dim3 grid, int order, bool perch, bool wide,
+                       hipStream_t s) {
   // per-channel scales are read once per lane, outside the pipeline
   const bool s16 = p.scales16 != nullptr && !perch;
   if (order == 0) {
-    if (perch) return launch_pipe_t<0, true, false>(p, grid, s);
-    return s16 ? launch_pipe_t<0, false, true>(p, grid, s) : launch_pipe_t<0, false, false>(p, grid, s);
+    if (perch) return launch_pipe_t<0, true, false>(p, grid, wide, s);
+    return s16 ? launch_pipe_t<0, false, true>(p, grid, wide, s)
+               : launch_pipe_t<0, false, false>(p, grid, wide, s);
   }
-  if (perch) return launch_pipe_t<1, true, false>(p, grid, s);
-  return s16 ? launch_pipe_t<1, false, true>(p, grid, s) : launch_pipe_t<1, false, false>(p, grid, s);
+  if (perch) return launch_pipe_t<1, true, false>(p, grid, wide, s);
+  return s16 ? launch_pipe_t<1, false, true>(p, grid, wide, s)
+             : launch_pipe_t<1, false, false>(p, grid, wide, s);
+}
+
+// 128 x 256 tiles for the pipelined kernel: only without split-K, and only
+// where 128 x 128 tiles would take more than one round of the chip's 256
+// CUs (then the wider tiles' cheaper steps outweigh the lost parallelism).
+bool pipe_wide(const GemmPlan& pl) {
+  return pl.split == 1 && (int64_t)pl.tiles_m * pl.tiles_n > 256;
 }
 
 template <int BN, int ORDER, int SMODE, bool QA4>
@@ -761,7 +820,6 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 2. the GEMM
-  const dim3 grid((unsigned)(pl.tiles_m * pl.tiles_n), 1, (unsigned)pl.split);
   // the branch-free kernel: power-of-two groups >= 32 or per-channel,
   // dword-aligned rows, K a multiple of 32 (each 16-byte weight chunk lies
   // wholly inside a row or wholly past its end: a vector load that crosses
@@ -776,10 +834,15 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
   const bool s16ok = !p.scales16 || smode == kPerChannel ||
                      (p.N % 2 == 0 && p.lds % 2 == 0 &&
                       reinterpret_cast<uintptr_t>(p.scales16) % 4 == 0);
-  if (qa4 && small && s16ok && p.K % 32 == 0 && (smode == kPerChannel || pow2))
-    e = launch_pipe(p, grid, order, smode == kPerChannel, s);
-  else
+  if (qa4 && small && s16ok && p.K % 32 == 0 && (smode == kPerChannel || pow2)) {
+    const bool wide = pipe_wide(pl);
+    if (wide) p.tiles_n = (int)((p.N + 255) / 256);
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), 1, (unsigned)pl.split);
+    e = launch_pipe(p, grid, order, smode == kPerChannel, wide, s);
+  } else {
+    const dim3 grid((unsigned)(pl.tiles_m * pl.tiles_n), 1, (unsigned)pl.split);
     e = launch_cfg<128>(p, grid, order, smode, qa4, s);
+  }
   if (e != hipSuccess || pl.split == 1) return e;
   // 3. split-K partial sums, in split order
   return launch_splitk_reduce(p.partial, p.bias, p.out, p.ldo, p.M, p.N, p.split, s);

@@ -170,6 +170,42 @@ def test_pipelined_gemm_output_stores(M, K, N, gs, pad_out):
                pad=(0, 0, 0, pad_out), label="pipe-stores")
 
 
+# ---- the pipelined GEMM's 128 x 256 tiles --------------------------------
+# Without split-K, and where 128 x 128 tiles would number more than 256, the
+# pipelined kernel runs 128 x 256 tiles (two 32-column blocks per wave, the
+# tile leaving in two passes).  Each shape below has more than 256 narrow
+# tiles and no split, a last wide tile that is partly past N, and an M tail.
+@pytest.mark.parametrize("M,K,N,gs,order,pad_out", [
+    (136, 256, 16400, 32, "low_first", 3),    # element stores (pitch 16403)
+    (390, 256, 8300, 128, "high_first", 0),   # 16-byte stores, last quad whole
+    (333, 256, 12290, 0, "low_first", 0),     # per-channel scales, last quad ragged
+])
+def test_pipelined_gemm_wide_tiles(M, K, N, gs, order, pad_out):
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=True, seed=M + N)
+    check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
+               pad=(0, 0, 0, pad_out), label="pipe-wide")
+
+
+def test_pipelined_gemm_wide_tiles_binary16_scales():
+    """q4f16_1 weights on the 128 x 256 tiles: the same values as fp32 scales
+    holding the binary16 values, bit for bit, and within the MFMA bound of
+    the oracle."""
+    need_gpu()
+    dev = torch.device("cuda")
+    M, K, N = 300, 512, 11000
+    x, qw, s, bias = inputs(M, K, N, 64, bias=True, seed=7)
+    s16 = s.half()
+    xd, qd, bd = x.to(dev), qw.to(dev), bias.to(dev)
+    o16 = b.linear(xd, qd, s16.to(dev), bd, K=K, group_size=64, math="f16")
+    o32 = b.linear(xd, qd, s16.float().to(dev), bd, K=K, group_size=64, math="f16")
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32)
+    ref, den = oracle_full(x, qw, s16.float(), bias, K=K, gs=64, order="low_first")
+    err = normalised_error(o16.cpu().numpy(), ref, den)
+    assert err <= 2e-3, err
+
+
 @pytest.mark.parametrize("math,M,K,N", [
     ("f16", 130, 2048, 1030),   # pipelined GEMM, no split: the output's own stores
     ("f16", 64, 8192, 260),     # pipelined GEMM, split K: the reduce kernel's stores
