@@ -324,14 +324,21 @@ def copy_calibration(torch, mib=1024, reps=8):
 
 
 def gpu_clocks():
-    """Current shader and memory clocks of GPU 0 as rocm-smi reports them
-    (read in a child process; context for the timings), or None."""
-    import subprocess
+    """Current shader and memory clock levels of cuda:0 (the levels the
+    driver's sysfs files mark with '*'; context for the timings), or None.
+    Read as plain files: no helper program is started."""
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values()))
-        return {k.split()[0]: v.strip("()") for k, v in card.items() if "clock speed" in k}
+        import torch
+        pr = torch.cuda.get_device_properties(0)
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (
+            pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+        out = {}
+        for key, name in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+            with open(os.path.join(dev, name)) as f:
+                cur = [ln.split(":", 1)[1].replace("*", "").strip()
+                       for ln in f if ln.rstrip().endswith("*")]
+            out[key] = cur[0] if cur else None
+        return out
     except Exception:
         return None
 
