@@ -123,6 +123,18 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   pl.split = (int)((spans + 7) / 8);  // at most 8 span-waves per workgroup
   pl.waves_k = (int)((spans + pl.split - 1) / pl.split);
   pl.k_per_split = (int64_t)pl.waves_k * 2048;
+  // More than two activation rows want the low-batch kernel to hold them in
+  // one workgroup, whose LDS takes at most 8 / waves_k of them: with four
+  // span waves the weights would stream once per two rows.  K is then split
+  // in two, so two spans meet per workgroup and it holds four rows, for the
+  // cost of the reduce launch (measured on MI355X for 8192 x 2048 at M = 4:
+  // 15.8 -> 13.3 us; at M = 16: 54.5 -> 37.1 us).  Deeper K is left as it
+  // is: splitting 14336 x 4096 in four was slower at M = 3 and 4.
+  if (M > 2 && pl.split == 1 && pl.waves_k == 4) {
+    pl.split = 2;
+    pl.waves_k = 2;
+    pl.k_per_split = 4096;
+  }
   // Rows per wave and row groups per workgroup, from a sweep on MI355X over
   // the Llama-shaped projections: about four waves per workgroup, four rows
   // per wave unless that leaves fewer than 2048 waves (then two), eight

@@ -84,6 +84,9 @@ def test_f32_path_several_rows(M):
     (7, 2048, 1000, 0, "high_first"), (8, 4096, 257, 128, "low_first"),
     (9, 1024, 129, 64, "low_first"), (16, 2048, 300, 32, "high_first"),
     (6, 6000, 90, 32, "low_first"), (2, 20000, 64, 32, "low_first"),
+    # four spans of 2048 k at M > 2: K split in two, four rows per workgroup
+    (3, 8192, 301, 32, "high_first"), (16, 8192, 515, 32, "low_first"),
+    (11, 6200, 260, 0, "low_first"), (4, 7000, 130, 64, "high_first"),
 ])
 def test_lowbatch_f32(M, K, N, gs, order):
     """Weights read once for all M rows; held to the fp32 bar."""
