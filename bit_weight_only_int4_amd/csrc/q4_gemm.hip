@@ -489,8 +489,10 @@ gemm_pipe_kernel(const GemmParams p) {
     va[u] = (uint32_t)((row * p.x16_pitch + 8 * c) * 2);
   }
   // packed weights of column block u: lane -> column c0 + 32u + lane/2,
-  // 16-byte half lane & 1
-  uint32_t vq[2], vs[2];  // fixed bound: a lambda capturing a template-sized array loses its host stub
+  // 16-byte half lane & 1.  The arrays have a fixed bound (NI <= 2): with a
+  // bound taken from the template arguments, the lambda below that captures
+  // them leaves the kernel without its host-side launch stub.
+  uint32_t vq[2], vs[2];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
     vq[u] = (uint32_t)((n0 + c0 + 32 * u + (lane >> 1)) * p.ldq + 16 * (lane & 1));
