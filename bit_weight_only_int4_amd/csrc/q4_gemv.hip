@@ -36,6 +36,12 @@
 //    order, so results are deterministic.  With K split over grid.z the
 //    partial sums go to the workspace and a second kernel adds them in split
 //    order.
+//  * Deep K (four or more spans) and very large single-span shapes run a
+//    second, streaming kernel instead (gemv_stream_kernel): each workgroup
+//    stages the activations once and its waves loop over row blocks, every
+//    wave covering all of K for its rows, with the next step's loads in
+//    flight while one computes.  No span waves meet in LDS and no split-K
+//    reduce runs for K <= 16384.
 //
 // Pages cited by number (the texts this layer is written from):
 //   page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"
@@ -165,6 +171,31 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size)
   return pl.split > 1 ? (size_t)pl.split * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+// The streaming kernel's domain: one activation row; K a multiple of 32
+// (every 16-byte chunk of a row lies inside the row or wholly past its
+// end) and at most 8 spans of 2048 (the activations fit its LDS);
+// dword-aligned weight rows; power-of-two groups of 32 .. 2048 or
+// per-channel scales, binary16 pairs dword-aligned; every byte offset
+// below 2^32 (its buffer resources).  Other one-row shapes run
+// gemv_f32_kernel.
+static bool use_stream(const GemvParams& p, int smode, bool qa4) {
+  if (p.M != 1 || !qa4 || p.K % 32 != 0 || p.K > 8 * 2048) return false;
+  // where it measured faster than gemv_f32_kernel on MI355X: deep K (four
+  // or more spans: no span waves meeting in LDS) or very many weights (the
+  // 2048 x 128257 output head); at the 1B projections' other sizes the
+  // one-pass kernel, whose every load is in flight from the start, is faster
+  if (!(p.K >= 4 * 2048 || (double)p.N * (double)p.K >= (double)(1 << 27))) return false;
+  if (smode != kStaged && smode != kPerChannel) return false;
+  if (p.scales16 && smode == kStaged &&
+      (p.lds % 2 != 0 || reinterpret_cast<uintptr_t>(p.scales16) % 4 != 0))
+    return false;
+  const uint64_t sb = p.scales16 ? 2 : 4;
+  const uint64_t scale_bytes =
+      smode == kPerChannel ? (uint64_t)p.N * sb : ((uint64_t)(p.G - 1) * p.lds + p.N) * sb;
+  return (uint64_t)p.N * (uint64_t)p.ldq < (1ull << 32) && scale_bytes < (1ull << 32) &&
+         (uint64_t)p.N * 4 < (1ull << 31);
+}
+
 hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s) {
   GemvParams p = p0;
   const GemvPlan pl = plan_gemv(p.M, p.N, p.K, p.group_size);
@@ -197,6 +228,25 @@ hipError_t launch_gemv(const GemvParams& p0, int order, bool qa4, hipStream_t s)
   l.grid = dim3((unsigned)((p.N + rpb - 1) / rpb), (unsigned)((p.M + mb - 1) / mb),
                 (unsigned)pl.split);
   l.R = R; l.mb = mb; l.xl = xl; l.order = order; l.smode = smode; l.qa4 = qa4; l.sa16 = sa16;
+  if (use_stream(p, smode, qa4)) {
+    // one activation row on aligned shapes: the streaming kernel (no split)
+    // One span over very many rows (the output head): four rows per wave
+    // step, four waves, one step in flight.  Deep K: two rows per step and
+    // two steps in flight, eight waves per workgroup, four when eight would
+    // leave CUs without a block (N < 4096).  Measured on MI355X against the
+    // other (waves, rows, depth) combinations on the Llama-shaped shapes.
+    const bool head = p.K <= 2048;
+    l.R = head ? 4 : 2;
+    l.waves = head || p.N < 4096 ? 4 : 8;
+    l.depth = head ? 1 : 2;
+    const int rows = l.waves * l.R;
+    p.spans = (int32_t)((p.K + 2047) / 2048);
+    p.blocks = (int32_t)((p.N + rows - 1) / rows);
+    p.split = 1;
+    l.stream = true;
+    l.grid = dim3((unsigned)(p.blocks < kStreamMaxGrid ? p.blocks : kStreamMaxGrid));
+    return p.scales16 ? launch_gemv_kernels<_Float16>(p, l, s) : launch_gemv_kernels<float>(p, l, s);
+  }
   const hipError_t e = p.scales16 ? launch_gemv_kernels<_Float16>(p, l, s)
                                   : launch_gemv_kernels<float>(p, l, s);
   if (e != hipSuccess || pl.split == 1) return e;

@@ -520,6 +520,228 @@ gemv_lb_kernel(const GemvParams p) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Streaming GEMV: one activation row, dword-aligned weight rows, K a multiple
+// of 32 and at most 8 spans of 2048, staged (power-of-two groups 32..2048)
+// or per-channel scales.  Every row a wave owns is traversed over the whole
+// of K by that wave, so no two waves meet to add partial sums:
+//  * A workgroup of W waves (4 or 8) stages the activations [0, 2048 S) in
+//    LDS once (zeros past K) and then loops over blocks of W * R
+//    rows: block b = L + i * gridDim.x for its XCD-ordered index L, so the
+//    blocks an XCD runs at once are neighbours and share the scale lines.
+//  * Inside a block, wave w owns rows R w .. R w + R - 1 (R = 2 or 4).  A
+//    wave step is one 2048-k span of its rows: lane l holds the 32 k at
+//    32 l, one 16-byte load per row (1 KiB per wave-wide load,
+//    non-temporal), and the scales of its chunk's group for all R rows in
+//    one load.
+//  * A ring of D wave steps (1 or 2): while one step computes, the loads of
+//    the next D - 1 are in flight, and the wave issues the loads D steps
+//    ahead before it adds up and stores the rows it has just finished.
+//  * Loads go through buffer resources that cover exactly the caller's
+//    arrays: past the last row (clamped) or the last scale they return zeros,
+//    which meet zero activations past K.
+// The arithmetic is that of gemv_f32_kernel (exact c, fp32 FMA chains, one
+// scale multiply per 32-k chunk, per-channel scales after the sum), so the
+// two give the same kind of fp32 result; their summation orders differ.
+// ---------------------------------------------------------------------------
+template <int R>
+struct StreamSlot {
+  uint32_t q[R][4];
+  float s[R];  // grouped: this lane's chunk scale for each row
+  float e;     // per-channel: lane r's row scale
+  float b;     // bias: lane r's row bias
+};
+
+// the R (2 or 4) consecutive scales at byte offset off, one load (fp32: 8 or
+// 16 bytes; binary16: 4 or 8 bytes, widened exactly)
+template <int R, typename ST>
+__device__ __forceinline__ void load_scale_row(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                               float (&s)[R]) {
+  static_assert(R == 2 || R == 4, "two or four rows per wave step");
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  if constexpr (sizeof(ST) == 4 && R == 2) {
+    const f2v v = __builtin_bit_cast(f2v, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+    s[0] = v.x; s[1] = v.y;
+  } else if constexpr (sizeof(ST) == 4) {
+    const f4 v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
+  } else if constexpr (R == 2) {
+    const h2 v = __builtin_bit_cast(h2, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    s[0] = (float)v.x; s[1] = (float)v.y;
+  } else {
+    const h4 v = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+    s[0] = (float)v.x; s[1] = (float)v.y; s[2] = (float)v.z; s[3] = (float)v.w;
+  }
+}
+
+template <typename ST>
+__device__ __forceinline__ float load_scale_one(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(ST) == 4)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  else
+    return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+}
+
+template <int W, int R, int ORDER, bool PERCH, bool ONESPAN, bool HASB, int D, typename ST>
+__global__ void __launch_bounds__(64 * W)
+gemv_stream_kernel(const GemvParams p) {
+  constexpr uint32_t SB = sizeof(ST);
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = ONESPAN ? 1 : p.spans;
+
+  // 1. the activations [0, 2048 S) into LDS (x_slot layout), zeros past K:
+  //    S * 8 wave-wide loads of 1 KiB spread over the waves
+  {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(uniform_ptr(p.x)), (short)0, (int)(p.K * 4), 0x00020000);
+    for (int i = wave; i < S * 8; i += W) {
+      const int j = i * 64 + lane;
+      const int span = j >> 9, l = (j >> 3) & 63, v = (j & 7) ^ ((l >> 1) & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_ptr_t)((char*)xs + i * 1024), 16,
+          (uint32_t)((span * 2048 + 32 * l + 4 * v) * 4), 0, 0, 0);
+    }
+  }
+
+  // 2. this wave's steps: blocks L, L + G, ... (G = gridDim.x), S spans each
+  const int G = (int)gridDim.x;
+  const int L = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+  const int T = ((p.blocks - L + G - 1) / G) * S;
+  const int64_t Kp = (p.K + 1) >> 1;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.qw), (short)0,
+      (int)(uint32_t)((uint64_t)(p.N - 1) * (uint64_t)p.ldq + (uint64_t)Kp), 0x00020000);
+  const ST* sp = scale_ptr<ST>(p);
+  const uint64_t sbytes = PERCH ? (uint64_t)p.N * SB
+                                : ((uint64_t)(p.G - 1) * (uint64_t)p.lds + (uint64_t)p.N) * SB;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<ST*>(sp), (short)0, (int)(uint32_t)sbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.bias), (short)0, (int)(p.N * 4), 0x00020000);
+  const uint32_t qlane = 16u * (uint32_t)lane;
+  // grouped: byte offset of this lane's chunk group in span 0, and per span
+  uint32_t slane = 0, sspan = 0;
+  if (!PERCH) {
+    slane = (uint32_t)(((32 * lane) >> p.log2_gs) * p.lds) * SB;
+    sspan = (uint32_t)((2048 >> p.log2_gs) * p.lds) * SB;
+  }
+  // The loads of step t (block i = t / S, span s = t % S).  Rows past N read
+  // row N - 1; lane l's per-row values (per-channel scale, bias) are those of
+  // row n0 + (l % R).  Steps past the wave's last one (issued so that every
+  // step issues the same loads) read lines of the activation row instead,
+  // spread over it and resident in L2: no weight traffic.
+  const __amdgpu_buffer_rsrc_t rx2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(uniform_ptr(p.x)), (short)0, (int)(p.K * 4), 0x00020000);
+  const uint32_t xspan = (uint32_t)(p.K * 4) & ~1023u;  // >= 1024: K >= 256 here
+  const uint32_t dlane = ((uint32_t)(wave * 1024 + 16 * lane)) % (xspan ? xspan : 1024u);
+  auto issue = [&](int t, StreamSlot<R>& sl) {
+    const bool live = t < T;
+    const int i = live ? t / S : 0, s = live ? t - i * S : 0;
+    const int n0 = ((L + i * G) * W + wave) * R;
+    const int nl = n0 + (lane & (R - 1)) < p.N ? n0 + (lane & (R - 1)) : (int)p.N - 1;
+    const __amdgpu_buffer_rsrc_t rq_ = live ? rq : rx2;
+    const __amdgpu_buffer_rsrc_t rs_ = live ? rs : rx2;
+    const __amdgpu_buffer_rsrc_t rb_ = live ? rb : rx2;
+    if (PERCH) sl.e = load_scale_one<ST>(rs_, live ? (uint32_t)nl * SB : dlane);
+    else load_scale_row<R, ST>(rs_, live ? (uint32_t)s * sspan + (uint32_t)n0 * SB + slane : dlane, sl.s);
+    if (HASB)
+      sl.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          rb_, live ? (uint32_t)nl * 4 : dlane, 0, 0));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = n0 + r < p.N ? n0 + r : (int)p.N - 1;
+      const uint32_t off = live ? (uint32_t)((uint64_t)n * (uint64_t)p.ldq) + (uint32_t)s * 1024u + qlane
+                                : dlane;
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 2));
+      sl.q[r][0] = v.x; sl.q[r][1] = v.y; sl.q[r][2] = v.z; sl.q[r][3] = v.w;
+    }
+  };
+
+  // A ring of D steps: while step t computes, the loads of steps t + 1 ..
+  // t + D - 1 are in flight.
+  StreamSlot<R> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    issue(j, ring[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // loads of a step: the scale (or per-channel scale), the bias, R rows; the
+  // activation loads were issued before all of them, so they have landed once
+  // no more than D steps' worth are outstanding
+  constexpr int PER = 1 + (HASB ? 1 : 0) + R;
+  asm volatile("" ::: "memory");
+  wait_vmcnt<D * PER>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  float xr[32];
+  auto load_x = [&](int s) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const f4 t = *reinterpret_cast<const f4*>(xs + 4 * x_slot(s, lane, v));
+      xr[4 * v + 0] = t.x; xr[4 * v + 1] = t.y; xr[4 * v + 2] = t.z; xr[4 * v + 3] = t.w;
+    }
+  };
+  if (ONESPAN) load_x(0);
+  const Magic mg = Magic::make();
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  // rows n0, n0 + 1 leave once their last span is in: the 64-lane sums,
+  // then lane r stores row n0 + r
+  auto finish = [&](int n0, float e, float b) {
+    float v = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float sum = wave_sum(acc[r]);
+      acc[r] = 0.0f;
+      v = lane == r ? sum : v;
+    }
+    if (PERCH) v *= e;
+    if (HASB) v += b;
+    if (lane < R && n0 + lane < p.N) p.out[n0 + lane] = v;
+  };
+
+  // Whole rounds of D steps, every step issuing the loads of the step D
+  // later (the same loads on every path keep the ring's registers in place
+  // across iterations, so the compiler waits for each slot only where it is
+  // used); steps past T compute nothing.
+  int s = 0, i = 0;
+  const int TR = (T + D - 1) / D * D;
+  for (int t0 = 0; t0 < TR; t0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int t = t0 + j;
+      const bool run = t < T;
+      float e = 0.0f, b = 0.0f;
+      bool last = false;
+      int n0 = 0;
+      if (run) {
+        if (!ONESPAN) load_x(s);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float dot = chunk_dot<ORDER>(ring[j].q[r], xr, mg);
+          acc[r] = PERCH ? acc[r] + dot : __builtin_fmaf(ring[j].s[r], dot, acc[r]);
+        }
+        e = ring[j].e;
+        b = ring[j].b;
+        last = s == S - 1;
+        n0 = ((L + i * G) * W + wave) * R;
+        if (++s == S) { s = 0; ++i; }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the loads D steps ahead go out before this block's sums and store
+      issue(t + D, ring[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (last) finish(n0, e, b);
+    }
+  }
+}
+
 template <int R, int ORDER, int SMODE, bool QA4, bool SA16, typename ST>
 hipError_t launch_t(const GemvParams& p, dim3 grid, bool xl, hipStream_t s) {
   const int nwaves = p.waves_k * p.waves_r;
@@ -576,10 +798,43 @@ hipError_t launch_r(const GemvParams& p, dim3 grid, bool xl, int order, int smod
   return hipErrorInvalidValue;
 }
 
+
+template <int W, int R, int ORDER, bool PERCH, int D, typename ST>
+hipError_t launch_stream_d(const GemvParams& p, dim3 grid, hipStream_t s) {
+  const size_t lds = (size_t)p.spans * 8192;
+  const dim3 block(64 * W);
+  if (p.spans == 1) {
+    if (p.bias) hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, true, true, D, ST>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, true, false, D, ST>), grid, block, lds, s, p);
+  } else {
+    if (p.bias) hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, false, true, D, ST>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, false, false, D, ST>), grid, block, lds, s, p);
+  }
+  return hipGetLastError();
+}
+
+// the three shapes the plan uses: (waves, rows, depth) = (8, 2, 2), (4, 2, 2)
+// and (4, 4, 1)
+template <int ORDER, bool PERCH, typename ST>
+hipError_t launch_stream_o(const GemvParams& p, const GemvLaunch& l, hipStream_t s) {
+  if (l.R == 4) return launch_stream_d<4, 4, ORDER, PERCH, 1, ST>(p, l.grid, s);
+  return l.waves == 8 ? launch_stream_d<8, 2, ORDER, PERCH, 2, ST>(p, l.grid, s)
+                      : launch_stream_d<4, 2, ORDER, PERCH, 2, ST>(p, l.grid, s);
+}
+
+template <typename ST>
+hipError_t launch_stream(const GemvParams& p, const GemvLaunch& l, hipStream_t s) {
+  const bool perch = l.smode == kPerChannel;
+  if (l.order == 0)
+    return perch ? launch_stream_o<0, true, ST>(p, l, s) : launch_stream_o<0, false, ST>(p, l, s);
+  return perch ? launch_stream_o<1, true, ST>(p, l, s) : launch_stream_o<1, false, ST>(p, l, s);
+}
+
 }  // namespace
 
 template <typename ST>
 hipError_t launch_gemv_kernels(const GemvParams& p, const GemvLaunch& l, hipStream_t s) {
+  if (l.stream) return launch_stream<ST>(p, l, s);
   if (l.mb > 1)
     return l.mb == 8   ? launch_lb<8, ST>(p, l.grid, l.R, l.order, l.smode, l.sa16, s)
            : l.mb == 4 ? launch_lb<4, ST>(p, l.grid, l.R, l.order, l.smode, l.sa16, s)

@@ -31,7 +31,14 @@ struct GemvParams {
   int32_t log2_gs;     // power-of-two group sizes: log2(group_size)
   int32_t waves_k;     // waves per workgroup along K (one 2048*CPL span each)
   int32_t waves_r;     // waves per workgroup along N (R rows each)
+  int32_t spans;       // streaming kernel: 2048-wide K spans (ceil(K / 2048))
+  int32_t blocks;      // streaming kernel: row blocks of (waves x rows per step) rows
 };
+
+// Streaming GEMV (one activation row, aligned shapes): the most workgroups
+// a launch runs; a workgroup block is (waves per workgroup) x (rows per wave
+// step) rows.
+constexpr int kStreamMaxGrid = 1024;
 
 struct GemvPlan {
   int cfg;            // chunks of 32 k per lane (1 or 2)
@@ -62,6 +69,9 @@ struct GemvLaunch {
   int smode;   // gemv::ScaleMode
   bool qa4;    // dword-aligned weight rows
   bool sa16;   // vector scale loads
+  bool stream; // the streaming kernel (grid.x workgroups loop over row blocks)
+  int depth;   // streaming kernel: wave steps in its load ring (1 or 2)
+  int waves;   // streaming kernel: waves per workgroup (4 or 8)
 };
 
 template <typename ST>
