@@ -25,7 +25,9 @@ DTYPES = {torch.float32: 0, torch.float16: 1}
 # exported symbols of include/q4linear.h
 SYMBOLS = ("q4_linear", "q4_linear_f16_scales", "q4_linear_workspace_bytes", "q4_linear_backward",
            "q4_linear_backward_workspace_bytes", "q4_requant", "q4_unpack_codes",
-           "q4_dequant", "q4_status_str", "q4_abi_version")
+           "q4_dequant", "q4_linear_noalloc", "q4_status_str", "q4_abi_version")
+ABI_VERSION = 2
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -56,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.q4_linear.restype = I32
     L.q4_linear_f16_scales.argtypes = L.q4_linear.argtypes
     L.q4_linear_f16_scales.restype = I32
+    L.q4_linear_noalloc.argtypes = [P, I, P, I, P, I, I, P, P, I, I, I, I, I32, I32, P, P]
+    L.q4_linear_noalloc.restype = I32
     L.q4_linear_workspace_bytes.argtypes = [I, I, I, I, I32]
     L.q4_linear_workspace_bytes.restype = SZ
     L.q4_unpack_codes.argtypes = [P, I, I, I, I32, P, I, P]
@@ -141,6 +145,38 @@ def linear(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
                ctypes.byref(path))
     if st != Q4_OK:
         raise Q4Error(st, entry.__name__)
+    return (out, PATHS[path.value]) if return_path else out
+
+
+def linear_noalloc(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
+                   bias: Optional[torch.Tensor] = None, *, out: torch.Tensor,
+                   K: Optional[int] = None, group_size: int, nibble_order: str = "low_first",
+                   math: str = "auto", return_path: bool = False):
+    """``linear`` through q4_linear_noalloc: no device memory is allocated
+    (the caller passes ``out``; the workspace is the library's own).  fp32
+    scales only, as that entry point takes."""
+    K = x.size(1) if K is None else K
+    ldx = _rows(x, "x", torch.float32)
+    ldq = _rows(qw, "qw", torch.uint8)
+    M, N = x.size(0), qw.size(0)
+    if group_size == 0:
+        if scales.dim() != 1 or scales.stride(0) != 1 or not scales.is_cuda \
+                or scales.dtype != torch.float32:
+            raise ValueError("per-channel scales must be a contiguous float32 device vector")
+        lds = N
+    else:
+        lds = _rows(scales, "scales", torch.float32)
+    if bias is not None:
+        if not bias.is_cuda or bias.dtype != torch.float32 or bias.dim() != 1 \
+                or bias.stride(0) != 1:
+            raise ValueError("bias must be a contiguous float32 device vector")
+    ldo = _rows(out, "out", torch.float32) if M > 0 and N > 0 else max(N, 1)
+    path = ctypes.c_int32(0)
+    st = lib().q4_linear_noalloc(_ptr(x), ldx, _ptr(qw), ldq, _ptr(scales), lds, group_size,
+                                 _ptr(bias), _ptr(out), ldo, M, N, K, ORDERS[nibble_order],
+                                 MATHS[math], _stream(), ctypes.byref(path))
+    if st != Q4_OK:
+        raise Q4Error(st, "q4_linear_noalloc")
     return (out, PATHS[path.value]) if return_path else out
 
 

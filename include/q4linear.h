@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 
 typedef int32_t q4_status;
 #define Q4_OK 0
@@ -252,6 +252,38 @@ q4_status q4_dequant(const uint8_t *qw, int64_t ldq, const float *scales,
                      int64_t lds, int64_t group_size, int64_t N, int64_t K,
                      int32_t nibble_order, int32_t dtype, void *w,
                      int64_t ldw, void *stream);
+
+/*
+ * q4_linear_noalloc -- q4_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, checks, kernels, results and
+ * Q4_PATH_* as q4_linear with the same sizes and math, without the
+ * workspace arguments: the workspace is a device array inside the library,
+ * Q4_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on (held from the load
+ * of the library's code object until the process ends).  The caller still
+ * passes x, qw, scales, bias and out.
+ *
+ * Runs on the current HIP device, which must be the device `stream`
+ * belongs to.  The first call on a device looks up that device's array
+ * (hipGetSymbolAddress); no call allocates or frees memory.
+ *
+ * Errors: those of q4_linear, and Q4_ERR_WORKSPACE when
+ * q4_linear_workspace_bytes(M, N, K, group_size, math) exceeds
+ * Q4_NOALLOC_SCRATCH_BYTES (nothing is queued); Q4_ERR_DEVICE when the
+ * device or its array cannot be found.
+ *
+ * Concurrency: every call on one GPU uses the same array.  Calls whose work
+ * overlaps in time on one GPU (different streams, or host threads queueing
+ * without ordering) race on it and give undefined results; calls queued in
+ * order on one stream do not.
+ */
+#define Q4_NOALLOC_SCRATCH_BYTES (64u << 20)
+q4_status q4_linear_noalloc(const float *x, int64_t ldx, const uint8_t *qw,
+                            int64_t ldq, const float *scales, int64_t lds,
+                            int64_t group_size, const float *bias, float *out,
+                            int64_t ldo, int64_t M, int64_t N, int64_t K,
+                            int32_t nibble_order, int32_t math, void *stream,
+                            int32_t *path_out);
 
 /* Static description of a status code. */
 const char *q4_status_str(q4_status status);

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     L = b.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.q4_abi_version() == 1
+    assert L.q4_abi_version() == b.ABI_VERSION
     for code, text in b.STATUS.items():
         assert L.q4_status_str(code).decode() == text
 
@@ -221,3 +221,40 @@ def test_f16_scale_entry_validates():
     # 8 groups x 128 binary16 scales end 2048 bytes after S
     assert call16(out=S + 2044)[0] == ALIAS
     assert call16(M=0, scales=None, x=None, qw=None, out=None) == (OK, 0)
+
+
+def call_noalloc(a):
+    path = ctypes.c_int32(-1)
+    st = b.lib().q4_linear_noalloc(a["x"], a["ldx"], a["qw"], a["ldq"], a["scales"], a["lds"],
+                                   a["gs"], a["bias"], a["out"], a["ldo"], a["M"], a["N"],
+                                   a["K"], a["order"], a["math"], a["stream"],
+                                   ctypes.byref(path))
+    return st, path.value
+
+
+@pytest.mark.parametrize("field,value", [
+    ("x", None), ("out", None), ("M", -1), ("K", 0), ("ldx", 255), ("order", 2), ("math", 3),
+])
+def test_noalloc_invalid_arguments(field, value):
+    # invalid sizes need no workspace, so q4_linear's checks report them
+    a = base_args(M=1)
+    a[field] = value
+    st, path = call_noalloc(a)
+    assert st == INVALID
+    assert path == 0
+
+
+def test_noalloc_rejects_workspace_beyond_its_array():
+    # 2048 x 32768 binary16 activations alone exceed the 64 MiB array: the
+    # call stops before looking up any device
+    need = b.lib().q4_linear_workspace_bytes(2048, 256, 32768, 32, 0)
+    assert need > b.NOALLOC_SCRATCH_BYTES
+    st, path = call_noalloc(base_args(M=2048, N=256, K=32768, ldx=32768, ldq=16384, lds=256,
+                                      ldo=256, bias=None))
+    assert st == WORKSPACE
+    assert path == 0
+
+
+def test_noalloc_empty_is_a_no_op():
+    assert call_noalloc(base_args(M=0))[0] == OK
+    assert call_noalloc(base_args(N=0))[0] == OK
