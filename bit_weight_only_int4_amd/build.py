@@ -4,10 +4,16 @@ Every source under ``csrc/`` is compiled with hipcc for gfx950 only, in
 parallel, then linked into one shared library beside this file.  No
 fast-math flags: fp32 denormals are kept and every operation rounds as IEEE
 specifies.  Packed fp32 instructions are disabled for the device code.
+
+Beside the library the build writes ``libq4linear.so.sha256``: a digest of
+the sources it was built from (comments and blank space removed), which the
+binding compares with the sources in the tree before it loads the library.
 """
 import concurrent.futures as cf
 import glob
+import hashlib
 import os
+import re
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -16,6 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libq4linear.so")
+TREE_LIB = LIB  # the in-tree library, whose stamp the binding checks
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -25,6 +32,38 @@ CFLAGS = [
     "-fno-gpu-rdc", "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and the C header with comments and blank
+    space removed: edits to comments alone keep it."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(INCLUDE, "q4linear.h")]
+    for f in files:
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(os.path.basename(f).encode())
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def stamp_path(lib: str) -> str:
+    return lib + ".sha256"
+
+
+def stale_reason(lib: str):
+    """None if the library's stamp matches the sources in the tree, else why
+    it does not."""
+    try:
+        with open(stamp_path(lib)) as f:
+            stamp = f.read().strip()
+    except OSError:
+        return "it has no source stamp (built by an older build script?)"
+    if stamp != source_digest():
+        return "it was built from other sources than those in the tree"
+    return None
 
 
 def _compile(src: str, verbose: bool) -> str:
@@ -52,8 +91,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
+    digest = source_digest()
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    with open(stamp_path(LIB), "w") as f:
+        f.write(digest + "\n")
     return LIB
 
 

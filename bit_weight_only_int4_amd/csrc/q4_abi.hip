@@ -133,12 +133,14 @@ q4_status linear_impl(const float* x, int64_t ldx, const uint8_t* qw, int64_t ld
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return Q4_ERR_INVALID_ARG;
   if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
     return Q4_ERR_INVALID_ARG;
-  if (math != Q4_MATH_AUTO && math != Q4_MATH_F32 && math != Q4_MATH_F16)
-    return Q4_ERR_INVALID_ARG;
+  if (math < Q4_MATH_AUTO || math > Q4_MATH_BF16) return Q4_ERR_INVALID_ARG;
   const int64_t Kp = (K + 1) / 2;
   const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
   if (ldx < K || ldq < Kp || ldo < N) return Q4_ERR_INVALID_ARG;
   if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
+  // a valid request this library has no kernels for: never a silent
+  // substitute
+  if (math == Q4_MATH_BF16) return Q4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return Q4_OK;
   // ---- pointer checks ----
   const void* scales = s16 ? (const void*)s16 : (const void*)s32;
@@ -160,7 +162,7 @@ q4_status linear_impl(const float* x, int64_t ldx, const uint8_t* qw, int64_t ld
   const size_t need = q4_linear_workspace_bytes(M, N, K, group_size, m);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return Q4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return Q4_ERR_WORKSPACE;
     const Range r_w{reinterpret_cast<uintptr_t>(workspace),
                     reinterpret_cast<uintptr_t>(workspace) + need};
     if (overlap(r_w, r_out) || overlap(r_w, r_x) || overlap(r_w, r_q) ||
@@ -244,12 +246,12 @@ q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw,
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return Q4_ERR_INVALID_ARG;
   if (nibble_order != Q4_ORDER_LOW_FIRST && nibble_order != Q4_ORDER_HIGH_FIRST)
     return Q4_ERR_INVALID_ARG;
-  if (math != Q4_MATH_AUTO && math != Q4_MATH_F32 && math != Q4_MATH_F16)
-    return Q4_ERR_INVALID_ARG;
+  if (math < Q4_MATH_AUTO || math > Q4_MATH_BF16) return Q4_ERR_INVALID_ARG;
   const int64_t Kp = (K + 1) / 2;
   const int64_t G = group_size == 0 ? 1 : (K + group_size - 1) / group_size;
   if (lddo < N || ldq < Kp || lddx < K) return Q4_ERR_INVALID_ARG;
   if (group_size > 0 && lds < N) return Q4_ERR_INVALID_ARG;
+  if (math == Q4_MATH_BF16) return Q4_ERR_UNSUPPORTED;
   const int32_t m = resolve_bwd_math(math, M, N, K, group_size);
   if (m == Q4_MATH_F16 && !bwd_mfma_groups(K, group_size)) return Q4_ERR_UNSUPPORTED;
   if (M == 0) return Q4_OK;
@@ -263,7 +265,7 @@ q4_status q4_linear_backward(const float* dout, int64_t lddo, const uint8_t* qw,
   const size_t need = q4_linear_backward_workspace_bytes(M, N, K, group_size, m);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return Q4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return Q4_ERR_WORKSPACE;
     const Range r_w{reinterpret_cast<uintptr_t>(workspace),
                     reinterpret_cast<uintptr_t>(workspace) + need};
     if (overlap(r_w, r_dx) || overlap(r_w, r_do) || overlap(r_w, r_q) || overlap(r_w, r_s))

@@ -18,7 +18,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "output overlaps an input",
           3: "workspace missing or too small", 4: "unsupported request",
           5: "HIP launch error"}
 ORDERS = {"low_first": 0, "high_first": 1}
-MATHS = {"auto": 0, "f32": 1, "f16": 2}
+MATHS = {"auto": 0, "f32": 1, "f16": 2, "bf16": 3}  # bf16: not built (Q4_ERR_UNSUPPORTED)
 PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16", 3: "bwd_f32", 4: "bwd_f16"}
 DTYPES = {torch.float32: 0, torch.float16: 1}
 
@@ -52,6 +52,12 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(
             f"HIP library {path} is not built; run "
             "`python -c 'import __graft_entry__ as g; g.build()'` first")
+    if os.path.abspath(path) == os.path.abspath(_build.TREE_LIB):
+        why = _build.stale_reason(path)
+        if why:
+            raise RuntimeError(
+                f"HIP library {path} does not match the sources: {why}; rebuild it "
+                "(`python -c 'import __graft_entry__ as g; g.build()'`)")
     L = ctypes.CDLL(path)
     P, I, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     L.q4_linear.argtypes = [P, I, P, I, P, I, I, P, P, I, I, I, I, I32, I32, P, SZ, P, P]
@@ -98,6 +104,42 @@ def _rows(t: torch.Tensor, name: str, dtype) -> int:
     return t.stride(0) if t.size(0) > 1 else max(t.size(1), t.stride(0))
 
 
+def _need(ok: bool, msg: str) -> None:
+    if not ok:
+        raise ValueError(msg)
+
+
+def _check_scales(scales: torch.Tensor, group_size: int, N: int, K: int) -> None:
+    if group_size == 0:
+        _need(scales.dim() == 1 and scales.numel() >= N,
+              f"per-channel scales need N = {N} entries, got shape {tuple(scales.shape)}")
+    elif group_size > 0:
+        G = -(-K // group_size)
+        _need(scales.dim() == 2 and scales.size(0) >= G and scales.size(1) >= N,
+              f"grouped scales need [ceil(K / group_size), N] = [{G}, {N}], "
+              f"got {tuple(scales.shape)}")
+
+
+def _check_linear_extents(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
+                          bias: Optional[torch.Tensor], out: Optional[torch.Tensor],
+                          K: int, group_size: int) -> None:
+    """Extents the C ABI does not see (it takes pitches, not sizes): an
+    undersized tensor is rejected here, before anything is queued, instead
+    of being read or written past its end."""
+    _need(x.dim() == 2, f"x must be 2-D [M, K], got shape {tuple(x.shape)}")
+    _need(x.size(1) >= K, f"x has {x.size(1)} columns, fewer than K = {K}")
+    _need(qw.dim() == 2 and qw.size(1) >= (K + 1) // 2,
+          f"qw needs [N, ceil(K / 2)] = [N, {(K + 1) // 2}] bytes, got {tuple(qw.shape)}")
+    M, N = x.size(0), qw.size(0)
+    _check_scales(scales, group_size, N, K)
+    if bias is not None:
+        _need(bias.dim() == 1 and bias.numel() >= N,
+              f"bias needs N = {N} entries, got shape {tuple(bias.shape)}")
+    if out is not None:
+        _need(tuple(out.shape) == (M, N), f"out must be [M, N] = [{M}, {N}], "
+                                          f"got {tuple(out.shape)}")
+
+
 def workspace_bytes(M: int, N: int, K: int, group_size: int, math: str = "auto") -> int:
     return int(lib().q4_linear_workspace_bytes(M, N, K, group_size, MATHS[math]))
 
@@ -115,6 +157,7 @@ def linear(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
     None.  Row strides of x, qw, scales and out are passed through as pitches.
     """
     K = x.size(1) if K is None else K
+    _check_linear_extents(x, qw, scales, bias, out, K, group_size)
     ldx = _rows(x, "x", torch.float32)
     ldq = _rows(qw, "qw", torch.uint8)
     M, N = x.size(0), qw.size(0)
@@ -156,6 +199,7 @@ def linear_noalloc(x: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor,
     (the caller passes ``out``; the workspace is the library's own).  fp32
     scales only, as that entry point takes."""
     K = x.size(1) if K is None else K
+    _check_linear_extents(x, qw, scales, bias, out, K, group_size)
     ldx = _rows(x, "x", torch.float32)
     ldq = _rows(qw, "qw", torch.uint8)
     M, N = x.size(0), qw.size(0)
@@ -201,6 +245,13 @@ def linear_backward(dout: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor, 
                     workspace: Optional[torch.Tensor] = None, return_path: bool = False):
     """dx[m, k] = sum_n dout[m, n] * (q[n, k] - 8) * s[g(k), n]: the input
     gradient of ``linear``.  dout [M, N] float32; qw and scales as in linear."""
+    _need(dout.dim() == 2 and qw.dim() == 2 and qw.size(1) >= (K + 1) // 2,
+          f"dout must be 2-D and qw [N, ceil(K / 2)] = [N, {(K + 1) // 2}] bytes, "
+          f"got {tuple(dout.shape)} and {tuple(qw.shape)}")
+    _check_scales(scales, group_size, qw.size(0), K)
+    if dx is not None:
+        _need(tuple(dx.shape) == (dout.size(0), K),
+              f"dx must be [M, K] = [{dout.size(0)}, {K}], got {tuple(dx.shape)}")
     lddo = _rows(dout, "dout", torch.float32)
     ldq = _rows(qw, "qw", torch.uint8)
     M, N = dout.size(0), qw.size(0)
@@ -228,8 +279,13 @@ def requant(latent: torch.Tensor, scales: torch.Tensor, *, group_size: int,
             nibble_order: str = "low_first", qw: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Packed codes [N, ceil(K/2)] uint8 of fp32 latent weights [N, K]:
     clamp(round(latent / s), -8, 7) + 8, zero scale -> 8."""
-    ldl = _rows(latent, "latent", torch.float32)
+    _need(latent.dim() == 2, f"latent must be 2-D [N, K], got {tuple(latent.shape)}")
     N, K = latent.shape
+    _check_scales(scales, group_size, N, K)
+    if qw is not None:
+        _need(qw.dim() == 2 and qw.size(0) == N and qw.size(1) >= (K + 1) // 2,
+              f"qw must be [N, >= ceil(K / 2)] = [{N}, >= {(K + 1) // 2}], got {tuple(qw.shape)}")
+    ldl = _rows(latent, "latent", torch.float32)
     lds = _scales_pitch(scales, group_size, N)
     if qw is None:
         qw = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=latent.device)
@@ -243,6 +299,8 @@ def requant(latent: torch.Tensor, scales: torch.Tensor, *, group_size: int,
 
 def unpack_codes(qw: torch.Tensor, K: int, nibble_order: str = "low_first") -> torch.Tensor:
     """Signed codes q - 8 as int8 [N, K]."""
+    _need(qw.dim() == 2 and qw.size(1) >= (K + 1) // 2,
+          f"qw needs [N, ceil(K / 2)] = [N, {(K + 1) // 2}] bytes, got {tuple(qw.shape)}")
     ldq = _rows(qw, "qw", torch.uint8)
     N = qw.size(0)
     codes = torch.empty((N, K), dtype=torch.int8, device=qw.device)
@@ -256,6 +314,9 @@ def unpack_codes(qw: torch.Tensor, K: int, nibble_order: str = "low_first") -> t
 def dequant(qw: torch.Tensor, scales: torch.Tensor, K: int, group_size: int,
             nibble_order: str = "low_first", dtype=torch.float32) -> torch.Tensor:
     """Dequantized weight [N, K]: float32 RN32((q-8)*s) or float16 RN16((q-8)*RN16(s))."""
+    _need(qw.dim() == 2 and qw.size(1) >= (K + 1) // 2,
+          f"qw needs [N, ceil(K / 2)] = [N, {(K + 1) // 2}] bytes, got {tuple(qw.shape)}")
+    _check_scales(scales, group_size, qw.size(0), K)
     ldq = _rows(qw, "qw", torch.uint8)
     N = qw.size(0)
     lds = N if group_size == 0 else _rows(scales, "scales", torch.float32)

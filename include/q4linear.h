@@ -24,8 +24,10 @@
  *     default stream).  Results are valid once the stream reaches that point;
  *     inputs must stay alive until then.
  *   - Row pitches (ldx, ldq, lds, ldo, ldc, ldw) are in ELEMENTS of the
- *     array's type (bytes for qw and codes).  Only natural element alignment
- *     is required; any pitch >= the row width is accepted.
+ *     array's type (bytes for qw and codes).  Operands need only natural
+ *     element alignment; any pitch >= the row width is accepted.  A
+ *     workspace must be 16-byte aligned (its kernels read and write it in
+ *     16-byte pieces), else the call returns Q4_ERR_WORKSPACE.
  *   - All arguments are checked before anything is queued; on any non-OK
  *     status no memory is read or written.  Errors are return codes; no C++
  *     exception crosses this boundary.
@@ -59,7 +61,8 @@ typedef int32_t q4_status;
 #define Q4_ERR_INVALID_ARG 1  /* NULL pointer, negative size, K <= 0, pitch
                                  below row width, unknown enum value */
 #define Q4_ERR_ALIAS 2        /* out overlaps an input */
-#define Q4_ERR_WORKSPACE 3    /* workspace NULL or smaller than required */
+#define Q4_ERR_WORKSPACE 3    /* workspace NULL, smaller than required or
+                                 not 16-byte aligned */
 #define Q4_ERR_UNSUPPORTED 4  /* a valid request the library does not implement */
 #define Q4_ERR_DEVICE 5       /* the HIP runtime reported a launch error */
 
@@ -76,6 +79,9 @@ typedef int32_t q4_status;
 #define Q4_MATH_F32 1  /* pure fp32: f32 dequant, f32 products, f32 sums */
 #define Q4_MATH_F16 2  /* binary16 operands (x and dequantized w) on MFMA,
                           fp32 accumulation; never binary16 accumulation */
+#define Q4_MATH_BF16 3 /* bfloat16 operands: a valid request this library
+                          does not implement; every entry point that takes
+                          a math returns Q4_ERR_UNSUPPORTED for it */
 
 /* Kernel that ran (reported through path_out). */
 #define Q4_PATH_NONE 0      /* nothing queued (M == 0 or N == 0) */
@@ -106,8 +112,8 @@ typedef int32_t q4_status;
  *   nibble_order  Q4_ORDER_*
  *   math          Q4_MATH_*
  *   workspace     device scratch of at least q4_linear_workspace_bytes(...)
- *                 bytes (may be NULL when that is 0); its contents on entry
- *                 are ignored and on exit are undefined
+ *                 bytes, 16-byte aligned (may be NULL when that is 0); its
+ *                 contents on entry are ignored and on exit are undefined
  *   stream        hipStream_t or NULL
  *   path_out      if not NULL, receives the Q4_PATH_* that was queued
  *
@@ -189,9 +195,10 @@ q4_status q4_unpack_codes(const uint8_t *qw, int64_t ldq, int64_t N,
  *           Q4_ERR_UNSUPPORTED.
  *   workspace     device scratch of q4_linear_backward_workspace_bytes(...)
  *                 bytes for the same math (F32: partial sums over row blocks
- *                 of the weight; F16: binary16 dout and split partials), may
- *                 be NULL when that is 0; contents on entry ignored, on exit
- *                 undefined
+ *                 of the weight; F16: binary16 dout and split partials),
+ *                 16-byte aligned, may be NULL when that is 0; contents on
+ *                 entry ignored, on exit undefined
+ *   math == Q4_MATH_BF16 returns Q4_ERR_UNSUPPORTED.
  *   stream, path_out: as in q4_linear
  *
  * Sizes are validated as in q4_linear (K > 0).  M == 0 is a no-op; N == 0

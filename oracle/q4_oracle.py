@@ -41,6 +41,11 @@ def _load():
     if _lib is None:
         if not os.path.exists(_build.LIB):
             _build.build()
+        if os.path.abspath(_build.LIB) == os.path.abspath(_build.TREE_LIB):
+            why = _build.stale_reason(_build.LIB)
+            if why:
+                raise RuntimeError(f"oracle library {_build.LIB} does not match q4_oracle.c: "
+                                   f"{why}; rebuild it (oracle.build.build())")
         lib = ctypes.CDLL(_build.LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int64

@@ -60,7 +60,7 @@ def call(a):
     ("x", None), ("qw", None), ("scales", None), ("out", None),
     ("M", -1), ("N", -1), ("K", 0), ("K", -5), ("gs", -1),
     ("ldx", 255), ("ldq", 127), ("lds", 127), ("ldo", 127),
-    ("order", 2), ("order", -1), ("math", 3), ("math", -1),
+    ("order", 2), ("order", -1), ("math", 4), ("math", -1),
     ("x", X + 2), ("out", OUT + 1), ("scales", S + 3), ("bias", BIAS + 2),
     ("M", 1 << 31), ("N", 1 << 31), ("K", 1 << 31),
 ])
@@ -233,7 +233,7 @@ def call_noalloc(a):
 
 
 @pytest.mark.parametrize("field,value", [
-    ("x", None), ("out", None), ("M", -1), ("K", 0), ("ldx", 255), ("order", 2), ("math", 3),
+    ("x", None), ("out", None), ("M", -1), ("K", 0), ("ldx", 255), ("order", 2), ("math", 4),
 ])
 def test_noalloc_invalid_arguments(field, value):
     # invalid sizes need no workspace, so q4_linear's checks report them
@@ -258,3 +258,35 @@ def test_noalloc_rejects_workspace_beyond_its_array():
 def test_noalloc_empty_is_a_no_op():
     assert call_noalloc(base_args(M=0))[0] == OK
     assert call_noalloc(base_args(N=0))[0] == OK
+
+
+UNSUPPORTED = 4
+
+
+def test_bf16_math_is_unsupported_everywhere():
+    """Q4_MATH_BF16 is a valid request that is not built: every entry point
+    taking a math rejects it with Q4_ERR_UNSUPPORTED before queueing
+    anything, also for empty sizes; its workspace query is 0."""
+    L = b.lib()
+    assert call(base_args(math=3)) == (UNSUPPORTED, 0)
+    assert call(base_args(math=3, M=0)) == (UNSUPPORTED, 0)
+    assert call_noalloc(base_args(math=3)) == (UNSUPPORTED, 0)
+    assert L.q4_linear_workspace_bytes(4, 128, 256, 32, 3) == 0
+    path = ctypes.c_int32(-1)
+    st = L.q4_linear_f16_scales(X, 256, Q, 128, S, 128, 32, BIAS, OUT, 128, 4, 128, 256, 0, 3,
+                                None, 0, None, ctypes.byref(path))
+    assert (st, path.value) == (UNSUPPORTED, 0)
+    st = L.q4_linear_backward(0x70000000, 128, Q, 128, S, 128, 32, 0x80000000, 256, 2, 128,
+                              256, 0, 3, None, 0, None, ctypes.byref(path))
+    assert (st, path.value) == (UNSUPPORTED, 0)
+    assert L.q4_linear_backward_workspace_bytes(2, 128, 256, 32, 3) == 0
+
+
+def test_workspace_must_be_16_byte_aligned():
+    L = b.lib()
+    M, N, K = 1, 64, 65536
+    need = L.q4_linear_workspace_bytes(M, N, K, 32, 0)
+    a = base_args(M=M, N=N, K=K, ldx=K, ldq=K // 2, lds=N, ldo=N)
+    for off in (4, 8, 12):
+        a.update(ws=WS + off, ws_bytes=need + 64)
+        assert call(a)[0] == WORKSPACE, off

@@ -21,7 +21,7 @@ import torch
 
 from bit_weight_only_int4_amd import q4linear as b
 from bit_weight_only_int4_amd.workloads import CONFIGS, make_inputs, small_projection
-from tests.gpu_util import check_case, need_gpu, run_gpu, oracle_full, normalised_error
+from tests.gpu_util import check_case, log, need_gpu, run_gpu, oracle_full, normalised_error
 from tests.packing import pack
 
 pytestmark = pytest.mark.gpu
@@ -300,3 +300,25 @@ def test_empty_sizes_are_noops():
     s = torch.ones(2, 16, device=dev)
     out, path = b.linear(x, qw, s, group_size=32, return_path=True)
     assert out.shape == (0, 16) and path == "none"
+
+
+@pytest.mark.parametrize("M,K,N,gs", [(64, 8192, 2048, 32), (1, 20480, 512, 32),
+                                      (4, 8192, 1024, 32), (200, 1024, 640, 0)])
+def test_workspace_16_byte_aligned(M, K, N, gs):
+    """A workspace that is 16-byte but not 256-byte aligned is accepted and
+    gives the same bits as the allocator's (256-byte aligned) one."""
+    need_gpu()
+    p = small_projection(M, K, N, gs)
+    x, qw, s, bias = make_inputs(p, 7)
+    dev = torch.device("cuda")
+    xd, qd, sd = x.to(dev), qw.to(dev), s.to(dev)
+    need = b.workspace_bytes(M, N, K, gs)
+    assert need > 0
+    ref = b.linear(xd, qd, sd, None, K=K, group_size=gs)
+    buf = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws = buf[16:16 + need]
+    assert ws.data_ptr() % 256 == 16
+    out = b.linear(xd, qd, sd, None, K=K, group_size=gs, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[ws+16] M={M} K={K} N={N} gs={gs}")
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
