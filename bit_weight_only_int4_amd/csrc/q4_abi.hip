@@ -49,22 +49,30 @@ bool aligned(const void* p, uintptr_t a) {
 // sizes representable in the kernels' index arithmetic
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
-// Q4_MATH_AUTO: fp32 for M == 1 (the GEMV) and for a few activation rows
-// whose products are few (the low-batch GEMV reads the weights once per
-// block of rows and, measured on MI355X, beats the MFMA GEMM there, whose
-// pre-pass, launches and split-K reduce cost 10-25 us at small M); binary16
-// MFMA otherwise.  Measured over the Llama-shaped projections at
-// M = 2 .. 16: the fp32 kernel is faster for every M <= 16 with
-// M * N * K <= 2^26, and at M = 2 up to M * N * K = 2^30 (the lm_head
-// projection); beyond these the GEMM is faster or within 10%.  Sizes only,
-// so the workspace query and the call agree.
+// Q4_MATH_AUTO: fp32 for M == 1 (the GEMV); binary16 MFMA for M > 1, except
+// for the few very small products where the fp32 low-batch GEMV is faster.
+// Measured on MI355X over the Llama-shaped projections (rotating weight
+// copies, graph-launched): where the few-row MFMA kernel takes the shape
+// (M <= 32, K % 32 == 0, per-channel or power-of-two groups >= 32) it wins
+// from M = 3 up except at N * K = 2^22 (M <= 4), and at M = 2 from
+// N * K > 2^25 (the 8B gate/up and down projections, the lm_head).  Where it
+// does not take the shape the tiled GEMM's three launches cost 10-25 us at
+// small M, and the fp32 kernel stays the faster for M <= 16 with
+// M * N * K <= 2^26 and for M == 2 up to M * N * K = 2^30.  Sizes only, so
+// the workspace query and the call agree.
 int32_t resolve_math(int32_t math, int64_t M, int64_t N, int64_t K, int64_t group_size) {
   if (math != Q4_MATH_AUTO) return math;
   if (M == 1) return Q4_MATH_F32;
-  const bool staged = group_size == 0 || group_size >= K ||
-                      ((group_size & (group_size - 1)) == 0 && group_size >= 32 &&
-                       group_size <= 2048);
-  const double mnk = (double)M * (double)N * (double)K;
+  const bool perch = group_size == 0 || group_size >= K;
+  const bool pow2 = (group_size & (group_size - 1)) == 0 && group_size >= 32;
+  const bool staged = perch || (pow2 && group_size <= 2048);
+  const double nk = (double)N * (double)K;
+  if (M <= 32 && K % 32 == 0 && K >= 128 && (perch || pow2)) {
+    const bool tiny = (M <= 4 && nk <= (double)(1LL << 22)) ||
+                      (M == 2 && nk <= (double)(1LL << 25));
+    return staged && tiny ? Q4_MATH_F32 : Q4_MATH_F16;
+  }
+  const double mnk = (double)M * nk;
   const bool few = (M <= 16 && mnk <= (double)(1LL << 26)) ||
                    (M <= 2 && mnk <= (double)(1LL << 30));
   if (staged && K % 4 == 0 && few) return Q4_MATH_F32;
@@ -195,8 +203,9 @@ q4_status linear_impl(const float* x, int64_t ldx, const uint8_t* qw, int64_t ld
     p.scales = s32; p.scales16 = s16; p.lds = lds; p.group_size = group_size; p.G = G;
     p.bias = bias; p.out = out; p.ldo = ldo;
     p.M = M; p.N = N; p.K = K;
-    e = q4::launch_gemm(p, nibble_order, qa4, workspace, s);
-    if (path_out) *path_out = Q4_PATH_GEMM_F16;
+    bool skinny = false;
+    e = q4::launch_gemm(p, nibble_order, qa4, workspace, s, &skinny);
+    if (path_out) *path_out = skinny ? Q4_PATH_GEMM_F16_SKINNY : Q4_PATH_GEMM_F16;
   }
   return e == hipSuccess ? Q4_OK : Q4_ERR_DEVICE;
 }

@@ -772,16 +772,24 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   return pl;
 }
 
-// workspace: [binary16 activations x16 | split-K partials]
+// workspace: [binary16 activations x16 | split-K partials] for the tiled
+// kernel; the skinny kernel's split-K partials where it applies.  The query
+// knows the sizes only (not the pointers that decide between the two), so it
+// asks for the larger.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   const GemmPlan pl = plan_gemm(M, N, K, group_size);
   size_t b = align256((size_t)pl.x16_rows * (size_t)pl.x16_pitch * sizeof(_Float16));
   if (pl.split > 1) b += (size_t)pl.split * (size_t)M * (size_t)N * sizeof(float);
-  return b;
+  const size_t sk = skinny_workspace_bytes(M, N, K, group_size);
+  return b > sk ? b : sk;
 }
 
 hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspace,
-                       hipStream_t s) {
+                       hipStream_t s, bool* skinny) {
+  const SkinnyPlan sp = plan_skinny(p0.M, p0.N, p0.K, p0.group_size);
+  const bool sk = skinny_fits(p0, sp, qa4);
+  if (skinny) *skinny = sk;
+  if (sk) return launch_skinny(p0, sp, order, workspace, s);
   GemmParams p = p0;
   const GemmPlan pl = plan_gemm(p.M, p.N, p.K, p.group_size);
   p.split = pl.split;

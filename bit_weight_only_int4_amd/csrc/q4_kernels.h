@@ -114,8 +114,30 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
+// The GEMM a call runs: the skinny kernel where it applies, else the tiled
+// one.  *skinny (if not null) tells which.
 hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, void* workspace,
-                       hipStream_t s);
+                       hipStream_t s, bool* skinny = nullptr);
+
+// Few-row MFMA GEMM (q4_skinny.hip): 1 <= M <= 32, K % 32 == 0, per-channel
+// or power-of-two groups >= 32, dword-aligned weight rows.
+struct SkinnyPlan {
+  bool ok;          // the sizes are the kernel's
+  int mb;           // 16-row MFMA blocks (1 or 2)
+  int wn, wk;       // waves per workgroup along N (32 columns each) and along K
+  int split;        // K slices (grid.y); > 1 only when a slice's activations exceed LDS
+  int64_t k_slice;  // k per slice, a multiple of 128
+  int spw;          // 128-k steps per wave and column block
+  int64_t blocks;   // column blocks of 32 * wn columns
+  int grid;         // workgroups per slice (persistent over the column blocks)
+  int x_lds;        // LDS bytes of the binary16 activations of a slice
+  int red_lds;      // LDS bytes of the partial sums (wk > 1)
+};
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size);
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size);
+bool skinny_fits(const GemmParams& p, const SkinnyPlan& pl, bool qa4);
+hipError_t launch_skinny(const GemmParams& p, const SkinnyPlan& pl, int order, void* workspace,
+                         hipStream_t s);
 
 // stage exports
 hipError_t launch_unpack_codes(const uint8_t* qw, int64_t ldq, int64_t N,

@@ -19,7 +19,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "output overlaps an input",
           5: "HIP launch error"}
 ORDERS = {"low_first": 0, "high_first": 1}
 MATHS = {"auto": 0, "f32": 1, "f16": 2, "bf16": 3}  # bf16: not built (Q4_ERR_UNSUPPORTED)
-PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16", 3: "bwd_f32", 4: "bwd_f16"}
+PATHS = {0: "none", 1: "gemv_f32", 2: "gemm_f16", 3: "bwd_f32", 4: "bwd_f16",
+         5: "gemm_f16_skinny"}
 DTYPES = {torch.float32: 0, torch.float16: 1}
 
 # exported symbols of include/q4linear.h

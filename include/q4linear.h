@@ -71,11 +71,15 @@ typedef int32_t q4_status;
 #define Q4_ORDER_HIGH_FIRST 1 /* qcs4w packer: byte = (q[even k] << 4) | q[odd k] */
 
 /* Arithmetic of q4_linear. */
-#define Q4_MATH_AUTO 0 /* M == 1: F32 GEMV; small batches (M <= 16 with
-                          M * N * K <= 2^26, or M == 2 with M * N * K <= 2^30;
-                          power-of-two groups >= 32 or per-channel, K % 4 == 0):
-                          F32 low-batch GEMV; else F16 MFMA GEMM.  Decided on
-                          sizes alone. */
+#define Q4_MATH_AUTO 0 /* M == 1: F32 GEMV.  M > 1: F16 MFMA GEMM, except
+                          for very small products where the F32 low-batch
+                          GEMV is faster: with K % 32 == 0 and per-channel or
+                          power-of-two groups >= 32 (the few-row kernel's
+                          shapes), M <= 4 with N * K <= 2^22 or M == 2 with
+                          N * K <= 2^25; otherwise (power-of-two groups >= 32
+                          or per-channel, K % 4 == 0) M <= 16 with
+                          M * N * K <= 2^26 or M == 2 with M * N * K <= 2^30.
+                          Decided on sizes alone. */
 #define Q4_MATH_F32 1  /* pure fp32: f32 dequant, f32 products, f32 sums */
 #define Q4_MATH_F16 2  /* binary16 operands (x and dequantized w) on MFMA,
                           fp32 accumulation; never binary16 accumulation */
@@ -89,6 +93,12 @@ typedef int32_t q4_status;
 #define Q4_PATH_GEMM_F16 2  /* MFMA f16 x f16 -> f32 GEMM */
 #define Q4_PATH_BWD_F32 3   /* fp32 input gradient (q4_linear_backward) */
 #define Q4_PATH_BWD_F16 4   /* MFMA f16 x f16 -> f32 input gradient */
+#define Q4_PATH_GEMM_F16_SKINNY 5 /* the same arithmetic as Q4_PATH_GEMM_F16 from the
+                                     few-row kernel (M <= 32, K % 32 == 0,
+                                     per-channel or power-of-two groups >= 32,
+                                     dword-aligned weight rows): one launch
+                                     unless a row block's binary16 activations
+                                     exceed LDS */
 
 /* Element type of q4_dequant's output. */
 #define Q4_DTYPE_F32 0

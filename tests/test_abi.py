@@ -104,14 +104,21 @@ def test_workspace_is_required_when_the_plan_splits():
 
 
 # (M, K, N, group_size, runs an fp32 GEMV): the automatic choice at and
-# around the boundaries of its rule (M <= 16 with M*N*K <= 2^26, or M == 2
-# with M*N*K <= 2^30; staged or per-channel scales; K % 4 == 0)
+# around the boundaries of its rule.  Shapes of the few-row MFMA kernel
+# (K % 32 == 0, per-channel or power-of-two groups >= 32): fp32 only for
+# M <= 4 with N*K <= 2^22 or M == 2 with N*K <= 2^25.  Other shapes: fp32 for
+# M <= 16 with M*N*K <= 2^26 or M == 2 with M*N*K <= 2^30 (staged or
+# per-channel scales, K % 4 == 0).
 REGIME = [
     (1, 2048, 128257, 0, True), (1, 14336, 4096, 128, True),
-    (4, 2048, 8192, 32, True), (4, 2048, 8193, 32, False),
-    (16, 2048, 2048, 32, True), (16, 2048, 2049, 32, False), (17, 256, 64, 32, False),
-    (2, 2048, 262144, 0, True), (2, 2048, 262145, 0, False), (3, 2048, 128257, 0, False),
+    (4, 2048, 2048, 32, True), (4, 2048, 2049, 32, False), (5, 2048, 2048, 32, False),
+    (4, 2048, 300, 32, True), (3, 4096, 1024, 0, True), (3, 4096, 1025, 0, False),
+    (2, 2048, 16384, 32, True), (2, 2048, 16385, 32, False), (2, 2048, 128257, 0, False),
+    (3, 2048, 128257, 0, False), (32, 2048, 64, 32, False),
+    (16, 2040, 2048, 32, True), (16, 2040, 2100, 32, False), (17, 2040, 64, 32, False),
+    (2, 2040, 263100, 0, True), (2, 2040, 263200, 0, False),
     (4, 2048, 300, 8, False), (4, 2046, 300, 0, False), (4, 2048, 300, 48, False),
+    (4, 2040, 300, 32, True),
 ]
 
 

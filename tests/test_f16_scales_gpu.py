@@ -59,11 +59,15 @@ def _case(M, K, N, gs, *, order="low_first", math="auto", pad=(0, 0, 0, 0), bias
     (1, 65536, 64, 32, "low_first", "auto", (0, 0, 0, 0), "gemv_f32"),
     # low batch
     (4, 2048, 300, 32, "low_first", "auto", (0, 0, 0, 0), "gemv_f32"),
-    (7, 2048, 1000, 0, "high_first", "auto", (0, 0, 0, 0), "gemv_f32"),
+    (7, 2048, 1000, 0, "high_first", "f32", (0, 0, 0, 0), "gemv_f32"),
     (3, 4096, 257, 64, "high_first", "f32", (0, 0, 2, 0), "gemv_f32"),
     # low batch over four spans of K: K split in two, four rows per workgroup
-    (4, 8192, 515, 32, "low_first", "auto", (0, 0, 0, 0), "gemv_f32"),
+    (4, 8192, 515, 32, "low_first", "f32", (0, 0, 0, 0), "gemv_f32"),
     (12, 8192, 300, 128, "high_first", "f32", (0, 0, 2, 0), "gemv_f32"),
+    # few-row MFMA GEMM: per-channel, grouped with a scale pitch, K split
+    (7, 2048, 1000, 0, "high_first", "auto", (0, 0, 0, 0), "gemm_f16_skinny"),
+    (24, 4096, 600, 128, "low_first", "auto", (0, 0, 2, 0), "gemm_f16_skinny"),
+    (16, 8192, 301, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16_skinny"),
     # pipelined GEMM (aligned, even N and pitch), several tiles and ragged M
     (70, 1024, 136, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
     (130, 2048, 512, 64, "high_first", "f16", (0, 0, 0, 0), "gemm_f16"),

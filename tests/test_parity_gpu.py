@@ -125,12 +125,15 @@ def test_gemm_shapes(M, K, N, gs, order):
 
 @pytest.mark.parametrize("M,K,N,gs,expect", [
     (1, 2048, 300, 32, "gemv_f32"), (4, 2048, 300, 32, "gemv_f32"),
-    (4, 2048, 8192, 32, "gemv_f32"), (8, 2048, 8192, 32, "gemm_f16"),
-    (4, 8192, 2048, 32, "gemv_f32"), (6, 8192, 2048, 32, "gemm_f16"),
-    (16, 2048, 2048, 32, "gemv_f32"), (17, 2048, 300, 32, "gemm_f16"),
-    (2, 2048, 128257, 0, "gemv_f32"), (3, 2048, 128257, 0, "gemm_f16"),
-    (2, 14336, 4096, 128, "gemv_f32"), (3, 4096, 14336, 128, "gemm_f16"),
-    (4, 2048, 300, 8, "gemm_f16"),
+    (4, 2048, 2048, 32, "gemv_f32"), (2, 2048, 8192, 32, "gemv_f32"),
+    (2, 8192, 2048, 32, "gemv_f32"), (3, 2048, 8192, 32, "gemm_f16_skinny"),
+    (4, 2048, 8192, 32, "gemm_f16_skinny"), (8, 2048, 8192, 32, "gemm_f16_skinny"),
+    (5, 2048, 2048, 32, "gemm_f16_skinny"), (16, 2048, 2048, 32, "gemm_f16_skinny"),
+    (32, 2048, 300, 0, "gemm_f16_skinny"), (33, 2048, 300, 0, "gemm_f16"),
+    (2, 2048, 128257, 0, "gemm_f16_skinny"), (7, 2048, 128257, 0, "gemm_f16_skinny"),
+    (2, 14336, 4096, 128, "gemm_f16_skinny"), (3, 4096, 14336, 128, "gemm_f16_skinny"),
+    (4, 2048, 300, 8, "gemm_f16"), (4, 2040, 300, 32, "gemv_f32"),
+    (20, 2040, 300, 32, "gemm_f16"), (9, 2040, 2048, 32, "gemv_f32"),
 ])
 def test_auto_regime(M, K, N, gs, expect):
     """The automatic choice of kernel, and its parity at that kernel's bar."""

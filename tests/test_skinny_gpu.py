@@ -1,0 +1,185 @@
+"""GPU parity of the few-row MFMA GEMM (M <= 32) against the fp64 oracle,
+through the C ABI, and the boundary between it and the tiled GEMM.
+
+The kernel's plan depends on the sizes alone, so the shapes below are
+chosen to reach each of its regimes (derived from the plan's rules, stated
+beside each case):
+  * waves of a workgroup along K (wk = 8, 4, 2) and along N only (wk = 1),
+    the latter with several column blocks per persistent workgroup;
+  * a K whose last 128-k step is partial (K % 128 != 0);
+  * K split across workgroups when one row block's binary16 activations
+    exceed LDS (M = 16 and M = 32 at K = 8192), with the split-K reduce;
+  * staging of the activations in several rounds (M * K / 8 > 2048);
+  * ragged N, both nibble orders, per-channel and grouped scales (32, 128),
+    fp32 and binary16 scales, bias on and off, row pitches, and a NaN-poisoned
+    output with guard rows and columns.
+The bar is the MFMA path's: max |gpu - ref| / sum_k |x * w| <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_weight_only_int4_amd import q4linear as b
+from bit_weight_only_int4_amd.workloads import make_inputs, small_projection
+from tests.gpu_util import check_case, log, need_gpu, normalised_error, oracle_full, run_gpu
+from tests.packing import pack
+
+pytestmark = pytest.mark.gpu
+
+SKINNY = "gemm_f16_skinny"
+
+
+def inputs(M, K, N, gs, order="low_first", bias=False, seed=0):
+    p = small_projection(M, K, N, gs, order=order, has_bias=bias, x_dist=("uniform", -1, 1))
+    return make_inputs(p, seed)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 24, 32, 33, 64, 65])
+@pytest.mark.parametrize("order", ["low_first", "high_first"])
+@pytest.mark.parametrize("gs", [0, 32, 128])
+def test_rows_around_the_boundary(M, order, gs):
+    """M <= 32 runs the skinny kernel, M >= 33 the tiled GEMM; N = 1000 is
+    ragged against 16- and 32-column blocks (wk = 8 here)."""
+    need_gpu()
+    K, N = 2048, 1000
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 1), seed=M * 31 + gs)
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
+                            label="skinny-boundary")
+    assert path == (SKINNY if M <= 32 else "gemm_f16")
+
+
+@pytest.mark.parametrize("M,K,N,gs,note", [
+    (3, 256, 140000, 32, "wk=1, 547 blocks over 512 workgroups: two blocks on some"),
+    (5, 256, 40000, 0, "wk=2"),
+    (9, 2048, 20000, 128, "wk=4"),
+    (7, 2080, 300, 32, "K % 128 = 32: partial last step, wk=8 with spw=3 > 17/8"),
+    (20, 160, 77, 32, "two steps, the second partial; wk=2"),
+    (32, 2048, 256, 32, "activations staged in four rounds"),
+    (16, 8192, 300, 32, "K split over 2 workgroups + reduce"),
+    (32, 8192, 520, 128, "K split over 4 workgroups + reduce, 160 KiB of LDS"),
+    (4, 8192, 2048, 32, "the 1B down projection at M=4, one slice"),
+    (7, 2048, 8192, 0, "the 1B gate projection, per-channel"),
+    (1, 4096, 777, 32, "one row"),
+    (12, 128, 33, 32, "the smallest K"),
+])
+@pytest.mark.parametrize("order", ["low_first", "high_first"])
+def test_plan_regimes(M, K, N, gs, note, order):
+    need_gpu()
+    log(f"[skinny] {note}")
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(N % 2 == 0), seed=M + K + N)
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
+                            label="skinny-plan")
+    assert path == SKINNY
+
+
+@pytest.mark.parametrize("pad", [(5, 4, 3, 7), (1, 0, 2, 1), (0, 8, 0, 3)])
+def test_row_pitches(pad):
+    """x, scale and output pitches; dword-aligned weight pitches stay on the
+    skinny kernel."""
+    need_gpu()
+    x, qw, s, bias = inputs(11, 2048, 333, 32, bias=True, seed=17)
+    _, path, _ = check_case(x, qw, s, bias, K=2048, gs=32, order="low_first", math="f16",
+                            pad=pad, label="skinny-pitch")
+    assert path == SKINNY
+
+
+def test_unaligned_weight_rows_take_the_tiled_kernel():
+    need_gpu()
+    x, qw, s, bias = inputs(11, 2048, 333, 32, bias=True, seed=18)
+    _, path, _ = check_case(x, qw, s, bias, K=2048, gs=32, order="low_first", math="f16",
+                            pad=(0, 1, 0, 0), label="skinny-unaligned")
+    assert path == "gemm_f16"
+
+
+@pytest.mark.parametrize("M,K,gs", [(8, 2056, 32), (8, 2048, 64), (8, 2048, 48), (8, 2048, 16)])
+def test_other_shapes_take_the_tiled_kernel(M, K, gs):
+    """K % 32 != 0 and groups that are not powers of two >= 32 are the tiled
+    kernel's."""
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, 200, gs, seed=19)
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
+                            label="skinny-other")
+    assert path == (SKINNY if gs == 64 else "gemm_f16")
+
+
+@pytest.mark.parametrize("M,gs", [(7, 0), (24, 32), (5, 128)])
+def test_binary16_scales(M, gs):
+    """q4f16_1 weights: binary16 scales give the same operands (a binary16
+    scale is its own RN16), hence the same bits as their fp32 widening."""
+    need_gpu()
+    K, N = 2048, 600
+    x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=23)
+    dev = torch.device("cuda")
+    s16 = s.half()
+    xd, qd, bd = x.to(dev), qw.to(dev), bias.to(dev)
+    o16, p16 = b.linear(xd, qd, s16.to(dev), bd, K=K, group_size=gs, math="f16",
+                        return_path=True)
+    o32, p32 = b.linear(xd, qd, s16.float().to(dev), bd, K=K, group_size=gs, math="f16",
+                        return_path=True)
+    torch.cuda.synchronize()
+    assert p16 == p32 == SKINNY
+    assert torch.equal(o16.view(torch.int32), o32.view(torch.int32))
+    ref, den = oracle_full(x, qw, s16.float(), bias, K=K, gs=gs, order="low_first")
+    assert normalised_error(o16.cpu().numpy(), ref, den) <= 2e-3
+
+
+@pytest.mark.parametrize("M", [1, 7, 16, 32])
+def test_integer_case_is_exact(M):
+    """x in {-2..2}, scales 2^-6: every operand is exact in binary16 and every
+    partial sum exact in fp32, so the kernel equals the oracle bit for bit
+    (K % 128 != 0: the partial last step included)."""
+    need_gpu()
+    rng = np.random.default_rng(100 + M)
+    K, N = 2080, 301
+    raw = rng.integers(0, 16, size=(N, K))
+    x = torch.from_numpy(rng.integers(-2, 3, size=(M, K)).astype(np.float32))
+    qw = torch.from_numpy(pack(raw, "high_first"))
+    s = torch.full((K // 32, N), 2.0 ** -6)
+    bias = torch.from_numpy(rng.integers(-9, 10, size=N).astype(np.float32) * 2.0 ** -6)
+    out, path, guards = run_gpu(x, qw, s, bias, K=K, gs=32, order="high_first", math="f16")
+    ref, _ = oracle_full(x, qw, s, bias, K=K, gs=32, order="high_first")
+    assert path == SKINNY and guards
+    assert np.array_equal(out.astype(np.float64), ref)
+
+
+def test_bytes_past_k_do_not_reach_the_sum():
+    """The last 128-k step reads whole 16-byte chunks; those past K hold the
+    row pitch's padding (0xFF: code 15).  With scales of 30000 such a code
+    would dequantize to +inf in binary16, and inf * 0 = NaN; the kernel
+    replaces the words past K by code 8 (c = 0), so the result stays finite
+    and matches the oracle."""
+    need_gpu()
+    rng = np.random.default_rng(7)
+    M, K, N = 5, 2080, 100
+    raw = rng.integers(7, 10, size=(N, K))  # c in {-1, 0, 1}: |c * s| <= 30000
+    qw = torch.from_numpy(pack(raw, "low_first"))
+    x = torch.from_numpy(rng.uniform(-1, 1, size=(M, K)).astype(np.float32))
+    s = torch.full((K // 32, N), 30000.0)
+    out, path, guards = run_gpu(x, qw, s, None, K=K, gs=32, order="low_first", math="f16",
+                                pad=(0, 48, 0, 0))
+    ref, den = oracle_full(x, qw, s, None, K=K, gs=32, order="low_first")
+    assert path == SKINNY and guards
+    assert np.all(np.isfinite(out))
+    assert normalised_error(out, ref, den) <= 2e-3
+
+
+def test_all_eights_give_the_bias():
+    need_gpu()
+    M, K, N = 9, 1024, 333
+    x = torch.randn(M, K, generator=torch.Generator().manual_seed(3))
+    qw = torch.full((N, K // 2), 0x88, dtype=torch.uint8)
+    s = torch.rand(K // 32, N, generator=torch.Generator().manual_seed(4))
+    bias = torch.randn(N, generator=torch.Generator().manual_seed(5))
+    out, path, guards = run_gpu(x, qw, s, bias, K=K, gs=32, order="low_first", math="f16")
+    assert path == SKINNY and guards
+    assert np.array_equal(out, np.broadcast_to(bias.numpy(), (M, N)))
+
+
+def test_repeat_calls_are_bit_identical():
+    need_gpu()
+    for M, K, N, gs in ((7, 2048, 3000, 0), (32, 8192, 520, 128), (4, 256, 70000, 32)):
+        x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=29)
+        a, pa, _ = run_gpu(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16")
+        c, pc, _ = run_gpu(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16")
+        assert pa == pc == SKINNY
+        assert np.array_equal(a, c)
