@@ -124,11 +124,12 @@ hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, void* workspace
 struct SkinnyPlan {
   bool ok;          // the sizes are the kernel's
   int mb;           // 16-row MFMA blocks (1 or 2)
-  int wn, wk;       // waves per workgroup along N (32 columns each) and along K
+  int ni;           // 16-column MFMA blocks per wave (2 or 4)
+  int wn, wk;       // waves per workgroup along N (16 ni columns each) and along K
   int split;        // K slices (grid.y); > 1 only when a slice's activations exceed LDS
   int64_t k_slice;  // k per slice, a multiple of 128
   int spw;          // 128-k steps per wave and column block
-  int64_t blocks;   // column blocks of 32 * wn columns
+  int64_t blocks;   // column blocks of 16 * ni * wn columns
   int grid;         // workgroups per slice (persistent over the column blocks)
   int x_lds;        // LDS bytes of the binary16 activations of a slice
   int red_lds;      // LDS bytes of the partial sums (wk > 1)
@@ -138,6 +139,10 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_siz
 bool skinny_fits(const GemmParams& p, const SkinnyPlan& pl, bool qa4);
 hipError_t launch_skinny(const GemmParams& p, const SkinnyPlan& pl, int order, void* workspace,
                          hipStream_t s);
+template <int ORDER>
+hipError_t launch_skinny_kernels(const GemmParams& p, const SkinnyPlan& pl, bool perch,
+                                 hipStream_t s);
+// (instantiated for each nibble order in q4_skinny_o0.hip / q4_skinny_o1.hip)
 
 // stage exports
 hipError_t launch_unpack_codes(const uint8_t* qw, int64_t ldq, int64_t N,
