@@ -159,6 +159,15 @@ def _bwd_case(M, N, K, gs, order, *, pad=(0, 0, 0, 0), seed=0, all_eights=False,
     (16, 640, 512, 128, "low_first", (0, 0, 0, 0)),
     (33, 256, 300, 100, "low_first", (0, 0, 0, 0)),
     (1, 3, 1, 0, "low_first", (0, 0, 0, 0)),
+    # dword-aligned rows with K % 32 == 0 at one to three rows: per-channel,
+    # groups of 32 / 128 / 96 and 8 / 24; K past the last 512-k block; ragged
+    # N; several row blocks (partial sums and the reduce)
+    (1, 515, 2080, 0, "high_first", (0, 0, 0, 0)),
+    (2, 700, 1024, 96, "low_first", (2, 4, 1, 3)),
+    (2, 333, 4096, 128, "high_first", (0, 8, 0, 0)),
+    (3, 1000, 2048, 8, "low_first", (0, 0, 0, 0)),
+    (1, 4097, 512, 24, "high_first", (1, 0, 2, 0)),
+    (2, 64, 160, 32, "low_first", (0, 0, 0, 0)),
 ])
 def test_backward_parity(M, N, K, gs, order, pad):
     need_gpu()
@@ -301,6 +310,7 @@ def test_backward_f16_full_size_sampled(name):
     ("f16", 130, 600, 1032),   # MFMA gradient, no split over N
     ("f16", 64, 4096, 264),    # MFMA gradient, split over N (the reduce kernel's stores)
     ("f32", 3, 700, 1000),     # fp32 gradient
+    ("f32", 2, 700, 1024),     # fp32 gradient, aligned rows
 ])
 def test_backward_dx_not_16_byte_aligned(math, M, N, K):
     """d_x may start at any 4-byte boundary: a view one float into its
