@@ -62,6 +62,24 @@ constexpr int DEPTH = 3;        // steps of global loads in flight (general kern
 
 enum ScaleMode : int { kPerChannel = 0, kGroup32 = 1, kGroup8 = 2, kGeneric = 3 };
 
+// Output tile of logical workgroup `tile` (after xcd_swizzle: consecutive
+// logical ids share an XCD and its L2).  Tiles go in groups of up to
+// kGroupM row tiles: inside a group the row tile varies fastest, then the
+// column tile.  The 32 workgroups an XCD runs at once then cover at most 4
+// row tiles x 8 column tiles, so each row tile's binary16 activations and
+// each column tile's weights are fetched into that L2 a few times rather
+// than once per workgroup (with the row tile fastest over all of M, as at
+// M = 2048, every workgroup of an XCD read other activation rows).
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void tile_of(uint32_t tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const uint32_t span = (uint32_t)kGroupM * (uint32_t)tiles_n;
+  const uint32_t g = tile / span, r = tile - g * span;
+  const int left = tiles_m - (int)g * kGroupM;
+  const uint32_t gm = (uint32_t)(left < kGroupM ? left : kGroupM);
+  tm = (int)(g * kGroupM + r % gm);
+  tn = (int)(r / gm);
+}
+
 // x16[r * kp + k] = RN16(x[r, k']) for r < mp, k < kp, where inside each
 // group of 8 the k' follow the nibble order of the packed words (pairs
 // (i, i + 4)); rows >= M and k >= K are zero.  A thread converts 8
@@ -264,8 +282,8 @@ gemm_f16_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * PITCH];
 
   const uint32_t tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int tm = (int)(tile % (uint32_t)p.tiles_m);
-  const int tn = (int)(tile / (uint32_t)p.tiles_m);
+  int tm, tn;
+  tile_of(tile, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;
   const int z = blockIdx.z;
@@ -458,8 +476,8 @@ gemm_pipe_kernel(const GemmParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lb = lane >> 5;
   const uint32_t tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int tm = (int)(tile % (uint32_t)p.tiles_m);
-  const int tn = (int)(tile / (uint32_t)p.tiles_m);
+  int tm, tn;
+  tile_of(tile, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * (128 * NI);
   const int c0 = 32 * NI * w;  // first tile column of this wave
