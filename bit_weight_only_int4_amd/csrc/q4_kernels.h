@@ -119,18 +119,20 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size)
 hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, void* workspace,
                        hipStream_t s, bool* skinny = nullptr);
 
-// Few-row MFMA GEMM (q4_skinny.hip): 1 <= M <= 32, K % 32 == 0, per-channel
+// Few-row MFMA GEMM (q4_skinny.hip): 1 <= M <= 64, K % 32 == 0, per-channel
 // or power-of-two groups >= 32, dword-aligned weight rows.
 struct SkinnyPlan {
   bool ok;          // the sizes are the kernel's
-  int mb;           // 16-row MFMA blocks (1 or 2)
+  int mz;           // row blocks (of mrows rows) handled by separate workgroups
+  int mrows;        // rows per row block (M when mz == 1, else 32)
+  int mb;           // 16-row MFMA blocks per row block (1 or 2)
   int ni;           // 16-column MFMA blocks per wave (2 or 4)
   int wn, wk;       // waves per workgroup along N (16 ni columns each) and along K
   int split;        // K slices (grid.y); > 1 only when a slice's activations exceed LDS
   int64_t k_slice;  // k per slice, a multiple of 128
   int spw;          // 128-k steps per wave and column block
   int64_t blocks;   // column blocks of 16 * ni * wn columns
-  int grid;         // workgroups per slice (persistent over the column blocks)
+  int grid;         // workgroups per slice, a multiple of mz (persistent over the column blocks)
   int x_lds;        // LDS bytes of the binary16 activations of a slice
   int red_lds;      // LDS bytes of the partial sums (wk > 1)
 };

@@ -1,4 +1,4 @@
-// q4_skinny.hip -- the plan of the few-row MFMA GEMM (1 <= M <= 32) and its
+// q4_skinny.hip -- the plan of the few-row MFMA GEMM (1 <= M <= 64) and its
 // launch; the kernel and its design are in q4_skinny_kernels.h.
 #include "q4_kernels.h"
 
@@ -15,15 +15,26 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   SkinnyPlan pl{};
   const bool perch = group_size == 0 || group_size >= K;
   const bool pow2 = group_size >= 32 && (group_size & (group_size - 1)) == 0;
-  pl.ok = M >= 1 && M <= 32 && N >= 1 && K >= SK_STEP && K % 32 == 0 && (perch || pow2) &&
+  // Above 32 rows (two row blocks, each reading the weights) the kernel is
+  // taken where it was measured faster than the tiled GEMM on MI355X: at
+  // M = 64 on the Llama-3.2-1B projections (N * K <= 2^24: 11.0-17.4 us
+  // against 13.7-21.9), the 8B q projection (16.3 against 20.4) and the
+  // vocabulary-sized output head (71.6 against 83.5), not on the 8B gate/up
+  // and down projections (31.4 and 32.4 against 27.9 and 29.4).
+  const bool rows_ok = M <= 32 || (M <= 64 && ((double)N * (double)K <= (double)(1LL << 25) ||
+                                               N >= 65536));
+  pl.ok = M >= 1 && rows_ok && N >= 1 && K >= SK_STEP && K % 32 == 0 && (perch || pow2) &&
           K <= ((int64_t)1 << 24);
   if (!pl.ok) return pl;
-  pl.mb = M <= 16 ? 1 : 2;
+  // more than 32 rows: row blocks of 32 in separate workgroups
+  pl.mz = (int)((M + 31) / 32);
+  pl.mrows = pl.mz == 1 ? (int)M : 32;
+  pl.mb = pl.mrows <= 16 ? 1 : 2;
   pl.ni = 2;
   const int64_t red = (int64_t)SK_W * pl.ni * pl.mb * 4 * 64 * 4;  // bytes
   constexpr int64_t kLds = 160 * 1024;
   const int64_t steps = (K + SK_STEP - 1) / SK_STEP;
-  const int64_t per_step = (int64_t)SK_STEP * M * 2;
+  const int64_t per_step = (int64_t)SK_STEP * pl.mrows * 2;
   const int64_t max_steps = (kLds - red) / per_step;
   int64_t split = (steps + max_steps - 1) / max_steps;
   const int64_t sps = (steps + split - 1) / split;
@@ -44,10 +55,10 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   pl.red_lds = wk > 1 ? (int)red : 0;
   const int64_t lds = pl.x_lds + pl.red_lds;
   const int64_t occ = lds * 2 <= kLds ? 2 : 1;  // workgroups per CU
-  int64_t grid = 256 * occ / split;
+  int64_t grid = 256 * occ / split / pl.mz;  // workgroups per row block
   if (grid < 1) grid = 1;
   if (grid > pl.blocks) grid = pl.blocks;
-  pl.grid = (int)grid;
+  pl.grid = (int)(grid * pl.mz);
   return pl;
 }
 

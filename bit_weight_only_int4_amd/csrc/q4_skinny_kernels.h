@@ -1,4 +1,4 @@
-// q4_skinny_kernels.h -- MFMA GEMM for few activation rows (1 <= M <= 32) on
+// q4_skinny_kernels.h -- MFMA GEMM for few activation rows (1 <= M <= 64) on
 // gfx950: binary16 operands, fp32 accumulation, the arithmetic of the tiled
 // prefill GEMM (q4_gemm.hip):
 //
@@ -22,6 +22,10 @@
 //    A wave streams the packed weights of its 32 columns (two 16-column
 //    MFMA blocks) straight from HBM into registers with 16-byte loads, a
 //    ring of D steps deep, and unpacks every word once into B operands.
+//  * More than 32 rows go in row blocks of 32, each its own set of
+//    workgroups; neighbouring workgroups (one XCD) take the same columns for
+//    different row blocks, so the second read of the weights meets the
+//    first in that XCD's L2.
 //  * The eight waves of a workgroup split its column block along K when the
 //    columns are few (narrow N) and add their partial sums through LDS in a
 //    fixed order; with many columns every wave owns a column block and
@@ -109,7 +113,7 @@ __device__ __forceinline__ float sk_scale(__amdgpu_buffer_rsrc_t r, uint32_t off
 //   SC_CHANNEL: per-channel scales: B = c, the whole sum times s at the end.
 enum SkScale : int { SC_ELEM = 0, SC_STEP = 1, SC_CHANNEL = 2 };
 
-// MB: 16-row MFMA blocks (1: M <= 16, 2: M <= 32).  NI: 16-column blocks
+// MB: 16-row MFMA blocks per row block (1: <= 16 rows, 2: <= 32).  NI: 16-column blocks
 // per wave (2 or 4: 32 or 64 columns, NI 16-byte weight loads per lane and
 // step, every A operand shared by NI MFMAs).
 template <int ORDER, int SC, bool S16, bool HASB, int MB, int NI>
@@ -127,16 +131,25 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
   const int wkc = pl.wk;                 // waves along K
   const int wn = wave / wkc, wk = wave - wn * wkc;
   const int li = lane & 15, g = lane >> 4;
-  const int M = (int)p.M;
+  // Row blocks of pl.mrows rows (grid of pl.mz of them): logical workgroup L
+  // takes row block L % mz for good, and column blocks of the workgroups
+  // L / mz; neighbouring logical ids (one XCD) share their column blocks,
+  // so the weights they stream meet in that XCD's L2.
+  const int Gx = (int)gridDim.x;
+  const int Lall = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+  const int zm = Lall % pl.mz;
+  const int L = Lall / pl.mz;                // this workgroup's rank among Gb
+  const int Gb = Gx / pl.mz;                 // workgroups per row block
+  const int64_t mrow0 = (int64_t)zm * pl.mrows;
+  const int M = (int)(p.M - mrow0 < pl.mrows ? p.M - mrow0 : pl.mrows);  // rows here
+  const float* const xrows = p.x + mrow0 * p.ldx;
   const int64_t N = p.N, K = p.K;
   const int z = blockIdx.y;
   const int64_t kz0 = (int64_t)z * pl.k_slice;
   const int64_t kz1 = kz0 + pl.k_slice < K ? kz0 + pl.k_slice : K;
   const int sps = (int)((kz1 - kz0 + SK_STEP - 1) / SK_STEP);  // steps in this slice
   const int spw = pl.spw;                // steps per wave and column block
-  const int Gx = (int)gridDim.x;
-  const int L = (int)xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nblk = (int)((pl.blocks - L + Gx - 1) / Gx);  // column blocks of this workgroup
+  const int nblk = (int)((pl.blocks - L + Gb - 1) / Gb);  // column blocks of this workgroup
   const int T = nblk * spw;
 
   const int64_t Kp = (K + 1) >> 1;
@@ -151,7 +164,7 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
   // so that every step issues the same instructions and the ring's registers
   // stay put; they are never computed.
   const __amdgpu_buffer_rsrc_t rx =
-      sk_rsrc(sk_uniform(p.x), (uint64_t)K * 4);
+      sk_rsrc(sk_uniform(xrows), (uint64_t)K * 4);
   const uint32_t xspan = (uint32_t)(K * 4) & ~1023u;
   const uint32_t dlane = ((uint32_t)(wave * 1024 + 16 * lane)) % (xspan ? xspan : 1024u);
 
@@ -162,7 +175,7 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
     const int sidx = wk * spw + sw;
     const bool blive = i < nblk;  // a column block of this workgroup
     const bool live = blive && sidx < sps;
-    const int64_t nb = ((int64_t)(L + i * Gx) * pl.wn + wn) * (16 * NI);
+    const int64_t nb = ((int64_t)(L + i * Gb) * pl.wn + wn) * (16 * NI);
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
       const int64_t n = nb + 16 * u + li;
@@ -199,7 +212,7 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
   const int cpr = sps * 16;  // 8-k chunks per row
   const int total = M * cpr;
   const __amdgpu_buffer_rsrc_t rxa =
-      sk_rsrc(sk_uniform(p.x), ((uint64_t)(M - 1) * (uint64_t)p.ldx + (uint64_t)K) * 4);
+      sk_rsrc(sk_uniform(xrows), ((uint64_t)(M - 1) * (uint64_t)p.ldx + (uint64_t)K) * 4);
   constexpr int NT = 64 * SK_W;
   struct Stage {
     f4 v[4][2];
@@ -340,8 +353,8 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
   };
 
   // out[m, n] (+ bias) or the slice's partial, for element v of block (u, mb)
-  float* const dst = pl.split > 1 ? p.partial + (int64_t)z * M * N : p.out;
   const int64_t dpitch = pl.split > 1 ? N : p.ldo;
+  float* const dst = (pl.split > 1 ? p.partial + (int64_t)z * p.M * N : p.out) + mrow0 * dpitch;
   const bool addb = HASB && pl.split == 1;
   auto store = [&](int64_t nb, int u, int mb, int v, float val, float scale, float bias) {
     const int m = 16 * mb + 4 * g + v;
@@ -354,7 +367,7 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
   // K, each wave parks its sums in LDS; then wave wk of the column group
   // adds, for its share of the elements, the wkc partials in wave order.
   auto finish = [&](int i, const float (&scale)[NI], const float (&bias)[NI]) {
-    const int64_t nb = ((int64_t)(L + i * Gx) * pl.wn + wn) * (16 * NI);
+    const int64_t nb = ((int64_t)(L + i * Gb) * pl.wn + wn) * (16 * NI);
     if (wkc == 1) {
 #pragma unroll
       for (int u = 0; u < NI; ++u)

@@ -81,8 +81,13 @@ typedef int32_t q4_status;
                           M * N * K <= 2^26 or M == 2 with M * N * K <= 2^30.
                           Decided on sizes alone. */
 #define Q4_MATH_F32 1  /* pure fp32: f32 dequant, f32 products, f32 sums */
-#define Q4_MATH_F16 2  /* binary16 operands (x and dequantized w) on MFMA,
-                          fp32 accumulation; never binary16 accumulation */
+#define Q4_MATH_F16 2  /* binary16 operands on MFMA, fp32 accumulation;
+                          never binary16 accumulation.  A = RN16(x); B =
+                          RN16((q - 8) * RN16(s)), except in the few-row
+                          kernel where one scale covers a whole 128-k step
+                          (per-channel scales, groups >= 128): there B = q - 8
+                          exactly and the scale multiplies the step's fp32
+                          sum (no rounding of the product to binary16) */
 #define Q4_MATH_BF16 3 /* bfloat16 operands: a valid request this library
                           does not implement; every entry point that takes
                           a math returns Q4_ERR_UNSUPPORTED for it */
@@ -93,8 +98,9 @@ typedef int32_t q4_status;
 #define Q4_PATH_GEMM_F16 2  /* MFMA f16 x f16 -> f32 GEMM */
 #define Q4_PATH_BWD_F32 3   /* fp32 input gradient (q4_linear_backward) */
 #define Q4_PATH_BWD_F16 4   /* MFMA f16 x f16 -> f32 input gradient */
-#define Q4_PATH_GEMM_F16_SKINNY 5 /* the same arithmetic as Q4_PATH_GEMM_F16 from the
-                                     few-row kernel (M <= 32, K % 32 == 0,
+#define Q4_PATH_GEMM_F16_SKINNY 5 /* binary16 operands, fp32 sums, from the
+                                     few-row kernel (M <= 32, and M <= 64 when
+                                     N * K <= 2^25 or N >= 65536; K % 32 == 0,
                                      per-channel or power-of-two groups >= 32,
                                      dword-aligned weight rows): one launch
                                      unless a row block's binary16 activations

@@ -129,7 +129,8 @@ def test_gemm_shapes(M, K, N, gs, order):
     (2, 8192, 2048, 32, "gemv_f32"), (3, 2048, 8192, 32, "gemm_f16_skinny"),
     (4, 2048, 8192, 32, "gemm_f16_skinny"), (8, 2048, 8192, 32, "gemm_f16_skinny"),
     (5, 2048, 2048, 32, "gemm_f16_skinny"), (16, 2048, 2048, 32, "gemm_f16_skinny"),
-    (32, 2048, 300, 0, "gemm_f16_skinny"), (33, 2048, 300, 0, "gemm_f16"),
+    (32, 2048, 300, 0, "gemm_f16_skinny"), (33, 2048, 300, 0, "gemm_f16_skinny"),
+    (65, 2048, 300, 0, "gemm_f16"),
     (2, 2048, 128257, 0, "gemm_f16_skinny"), (7, 2048, 128257, 0, "gemm_f16_skinny"),
     (2, 14336, 4096, 128, "gemm_f16_skinny"), (3, 4096, 14336, 128, "gemm_f16_skinny"),
     (4, 2048, 300, 8, "gemm_f16"), (4, 2040, 300, 32, "gemv_f32"),

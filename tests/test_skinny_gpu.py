@@ -1,4 +1,4 @@
-"""GPU parity of the few-row MFMA GEMM (M <= 32) against the fp64 oracle,
+"""GPU parity of the few-row MFMA GEMM (M <= 64) against the fp64 oracle,
 through the C ABI, and the boundary between it and the tiled GEMM.
 
 The kernel's plan depends on the sizes alone, so the shapes below are
@@ -10,6 +10,7 @@ beside each case):
   * K split across workgroups when one row block's binary16 activations
     exceed LDS (M = 16 and M = 32 at K = 8192), with the split-K reduce;
   * staging of the activations in several rounds (M * K / 8 > 2048);
+  * more than 32 rows: row blocks of 32 in separate workgroups;
   * ragged N, both nibble orders, per-channel and grouped scales (32, 128),
     fp32 and binary16 scales, bias on and off, row pitches, and a NaN-poisoned
     output with guard rows and columns.
@@ -34,18 +35,35 @@ def inputs(M, K, N, gs, order="low_first", bias=False, seed=0):
     return make_inputs(p, seed)
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 24, 32, 33, 64, 65])
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 24, 32, 33, 48, 64, 65])
 @pytest.mark.parametrize("order", ["low_first", "high_first"])
 @pytest.mark.parametrize("gs", [0, 32, 128])
 def test_rows_around_the_boundary(M, order, gs):
-    """M <= 32 runs the skinny kernel, M >= 33 the tiled GEMM; N = 1000 is
-    ragged against 16- and 32-column blocks (wk = 8 here)."""
+    """M <= 64 runs the skinny kernel here (N * K <= 2^25; above 32 rows in
+    two row blocks), M >= 65 the tiled GEMM; N = 1000 is ragged against 16-
+    and 32-column blocks (wk = 8 here)."""
     need_gpu()
     K, N = 2048, 1000
     x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 1), seed=M * 31 + gs)
     _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
                             label="skinny-boundary")
-    assert path == (SKINNY if M <= 32 else "gemm_f16")
+    assert path == (SKINNY if M <= 64 else "gemm_f16")
+
+
+@pytest.mark.parametrize("M,K,N,gs,expect", [
+    (40, 4096, 14336, 128, "gemm_f16"),      # N * K > 2^25: the tiled GEMM
+    (33, 2048, 16384, 32, SKINNY),           # N * K = 2^25
+    (33, 2048, 16385, 32, "gemm_f16"),
+    (50, 2048, 70000, 0, SKINNY),            # vocabulary-sized N
+    (64, 8192, 2048, 32, SKINNY),            # two row blocks, K split over 4 + reduce
+    (41, 256, 3000, 32, SKINNY),             # two row blocks, the second of 9 rows
+])
+def test_two_row_blocks(M, K, N, gs, expect):
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=M + K + N)
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="high_first", math="f16",
+                            label="skinny-rows")
+    assert path == expect
 
 
 @pytest.mark.parametrize("M,K,N,gs,note", [
@@ -123,7 +141,7 @@ def test_binary16_scales(M, gs):
     assert normalised_error(o16.cpu().numpy(), ref, den) <= 2e-3
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 32])
+@pytest.mark.parametrize("M", [1, 7, 16, 32, 48, 64])
 def test_integer_case_is_exact(M):
     """x in {-2..2}, scales 2^-6: every operand is exact in binary16 and every
     partial sum exact in fp32, so the kernel equals the oracle bit for bit
