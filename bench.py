@@ -548,7 +548,10 @@ def traffic_run(torch, b, CONFIGS, make_inputs, wanted, order_path, calls_per=1)
     """calls_per calls per projection, back to back, each on a weight copy
     that later copies have pushed out of the caches (copies 1, 2, ...), the
     projections 30 ms apart, so a profiled run's dispatches of the library
-    fall into groups that map to the projections in order."""
+    fall into groups that map to the projections in order.  The 30 ms are a
+    spin kernel on the GPU, not a host sleep: an idle GPU drops its clocks,
+    and the first calls after an idle gap would run slower than the bench's
+    back-to-back steps."""
     order = []
     print("[bench] copy calibration", file=sys.stderr, flush=True)
     order.append(dict(config="copy", projection="copy", calibration=copy_calibration(torch)))
@@ -558,7 +561,7 @@ def traffic_run(torch, b, CONFIGS, make_inputs, wanted, order_path, calls_per=1)
         projs = pick(CONFIGS)
         suite = Suite(projs, torch, b, make_inputs)
         for i, p in enumerate(projs):
-            time.sleep(0.03)
+            gap(torch)
             for r in range(calls_per):
                 _, path = suite.launch(i, 1 + r % (suite.copies - 1), return_path=True)
             torch.cuda.synchronize()
@@ -567,9 +570,16 @@ def traffic_run(torch, b, CONFIGS, make_inputs, wanted, order_path, calls_per=1)
         print(f"[bench] {name}: one call per projection", file=sys.stderr, flush=True)
         del suite
         torch.cuda.empty_cache()
-    time.sleep(0.03)
+    gap(torch)
     with open(order_path, "w") as f:
         json.dump(order, f)
+
+
+def gap(torch, seconds=0.03):
+    """About `seconds` of GPU time in a spin kernel (torch.cuda._sleep counts
+    shader clock cycles, at most 2.4 GHz), then a synchronisation."""
+    torch.cuda._sleep(int(seconds * 2.4e9))
+    torch.cuda.synchronize()
 
 
 def _library_groups(events, ncalls, where):
