@@ -41,7 +41,11 @@
 //    stages the activations once and its waves loop over row blocks, every
 //    wave covering all of K for its rows, with the next step's loads in
 //    flight while one computes.  No span waves meet in LDS and no split-K
-//    reduce runs for K <= 16384.
+//    reduce runs for K <= 16384.  With one span (the output head) a lane's
+//    activation chunk serves every row its wave visits, so that kernel
+//    rewrites it once as block fixed point (27 bits against the chunk's
+//    largest |x|) and forms the products exactly with 4-bit integer dot
+//    products (q4_gemv_kernels.h describes the arithmetic).
 //
 // Pages cited by number (the texts this layer is written from):
 //   page 1: ExecuTorch PR #20815, "[WebGPU] Add 256-thread steel q4gsw prefill GEMM"

@@ -149,6 +149,98 @@ __device__ __forceinline__ float chunk_dot_generic(const uint32_t (&q)[4], const
   return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
+// ---------------------------------------------------------------------------
+// Integer inner products for the streaming GEMV.  A lane's 32-k activation
+// chunk is written as block fixed point: with E the binary exponent of the
+// chunk's largest |x| (2^(E-1) <= max |x| < 2^E), X_k = RN(x_k 2^(26 - E)),
+// |X_k| <= 2^26, i.e. 27 significant bits against the chunk's largest value.
+// Each X_k is split into seven balanced base-16 digits (-8..7, X_k =
+// sum_l d_l 16^l), stored as signed 4-bit fields, and the digits are
+// transposed so that register lim[l][d] holds digit l of the eight x of word
+// d in the nibble positions of that word's codes.  A packed word XOR 0x8 in
+// every nibble is its codes c = q - 8 as signed 4-bit fields, so
+// v_dot8_i32_i4 of the two gives sum over the word of c * d_l exactly; seven
+// of them per word, integer sums over the chunk, and
+//   sum_k c_k X_k = T_hi 2^16 + T_lo  (T_lo = sum_{l<4} S_l 16^l,
+//   T_hi = sum_{l>=4} S_l 16^(l-4), both exact in fp32)
+// is formed with one fp32 rounding and scaled by 2^(E - 26).  Per packed
+// word: 1 XOR and 7 dot products, against 9 unpack and 8 FMA instructions.
+// The chunk's largest |x| is taken over the bit patterns of |x|, where NaN
+// ranks above inf; a non-finite largest |x| becomes the chunk's factor, so
+// every row that meets the chunk gets a non-finite sum (inf or NaN; which
+// one, and the sign of an inf, may differ from an fp32 sum over the same
+// products).
+// ---------------------------------------------------------------------------
+
+// 8 x 8 transpose of 4-bit fields: afterwards R[l] nibble i = (before) R[i]
+// nibble l.  Three exchange stages: 16-bit halves between rows i, i + 4;
+// bytes between rows i, i + 2; nibbles between rows i, i + 1.
+__device__ __forceinline__ void nibble_transpose(uint32_t (&R)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = R[i], b = R[i + 4];
+    R[i] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    R[i + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = (t & 1) + 4 * (t >> 1);
+    const uint32_t a = R[i], b = R[i + 2];
+    R[i] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+    R[i + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t a = R[i], b = R[i + 1];
+    R[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    R[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+// the chunk x (k order of the lane's 32 k) as digits lim and factor e
+template <int ORDER>
+__device__ __forceinline__ void chunk_digits(const float (&x)[32], uint32_t (&lim)[7][4],
+                                             float& e) {
+  uint32_t mb = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t a = __builtin_bit_cast(uint32_t, x[k]) & 0x7FFFFFFFu;
+    mb = mb > a ? mb : a;
+  }
+  const float m = __builtin_bit_cast(float, mb);
+  const int E = __builtin_amdgcn_frexp_expf(m);  // 0 for m = 0
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int X = (int)__builtin_rintf(__builtin_ldexpf(x[8 * d + nibble_k<ORDER>(i)], 26 - E));
+      // balanced digits: nibble l of X + 0x08888888 is d_l + 8; XOR 8 gives
+      // d_l as a signed 4-bit field
+      R[i] = ((uint32_t)X + 0x08888888u) ^ 0x08888888u;
+    }
+    nibble_transpose(R);
+#pragma unroll
+    for (int l = 0; l < 7; ++l) lim[l][d] = R[l];
+  }
+  e = __builtin_isfinite(m) ? __builtin_ldexpf(1.0f, E - 26) : m;
+}
+
+// sum over one chunk of c_k X_k (four packed words), one fp32 rounding
+__device__ __forceinline__ float chunk_dot_digits(const uint32_t (&q)[4],
+                                                  const uint32_t (&lim)[7][4]) {
+  int S[7] = {0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int c = (int)(q[d] ^ 0x88888888u);
+#pragma unroll
+    for (int l = 0; l < 7; ++l) S[l] = __builtin_amdgcn_sdot8(c, (int)lim[l][d], S[l], false);
+  }
+  const int lo = S[0] + 16 * (S[1] + 16 * (S[2] + 16 * S[3]));
+  const int hi = S[4] + 16 * (S[5] + 16 * S[6]);
+  return __builtin_fmaf((float)hi, 65536.0f, (float)lo);
+}
+
 // Sum over the 64 lanes of a wave with DPP row operations (quad swaps, half
 // row and row mirrors, then the gfx9 row broadcasts); lane 63 ends with the
 // total, which is returned wave-uniform.
@@ -583,9 +675,11 @@ __device__ __forceinline__ float load_scale_one(__amdgpu_buffer_rsrc_t rs, uint3
     return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
 }
 
-template <int W, int R, int ORDER, bool PERCH, bool ONESPAN, bool HASB, int D, typename ST>
+template <int W, int R, int ORDER, bool PERCH, bool ONESPAN, bool HASB, int D, typename ST,
+          bool IDOT = false>
 __global__ void __launch_bounds__(64 * W)
 gemv_stream_kernel(const GemvParams p) {
+  static_assert(!IDOT || ONESPAN, "integer products: one span, digits formed once");
   constexpr uint32_t SB = sizeof(ST);
   extern __shared__ __attribute__((aligned(16))) float xs[];
   const int lane = threadIdx.x & 63;
@@ -687,6 +781,10 @@ gemv_stream_kernel(const GemvParams p) {
   };
   if (ONESPAN) load_x(0);
   const Magic mg = Magic::make();
+  // integer products: the lane's chunk as digits, formed once
+  uint32_t lim[7][4];
+  float xe = 0.0f;
+  if constexpr (IDOT) chunk_digits<ORDER>(xr, lim, xe);
 
   float acc[R];
 #pragma unroll
@@ -724,7 +822,8 @@ gemv_stream_kernel(const GemvParams p) {
         if (!ONESPAN) load_x(s);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float dot = chunk_dot<ORDER>(ring[j].q[r], xr, mg);
+          const float dot = IDOT ? chunk_dot_digits(ring[j].q[r], lim) * xe
+                                 : chunk_dot<ORDER>(ring[j].q[r], xr, mg);
           acc[r] = PERCH ? acc[r] + dot : __builtin_fmaf(ring[j].s[r], dot, acc[r]);
         }
         e = ring[j].e;
@@ -804,8 +903,8 @@ hipError_t launch_stream_d(const GemvParams& p, dim3 grid, hipStream_t s) {
   const size_t lds = (size_t)p.spans * 8192;
   const dim3 block(64 * W);
   if (p.spans == 1) {
-    if (p.bias) hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, true, true, D, ST>), grid, block, lds, s, p);
-    else hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, true, false, D, ST>), grid, block, lds, s, p);
+    if (p.bias) hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, true, true, D, ST, true>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, true, false, D, ST, true>), grid, block, lds, s, p);
   } else {
     if (p.bias) hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, false, true, D, ST>), grid, block, lds, s, p);
     else hipLaunchKernelGGL((gemv_stream_kernel<W, R, ORDER, PERCH, false, false, D, ST>), grid, block, lds, s, p);
