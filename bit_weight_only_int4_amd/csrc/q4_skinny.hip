@@ -47,15 +47,34 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   for (int c = 1; c <= 8; c *= 2)
     if ((ncb * c + 7) / 8 >= 256) { wk = c; break; }
   while (wk > 1 && wk > sps) wk /= 2;
+  const int64_t blocks = (ncb + SK_W / wk - 1) / (SK_W / wk);
+  // Narrow N over deep K (the down projections at few rows) leaves CUs
+  // without a block even with all 8 waves along K: split K further, while
+  // every wave keeps at least two steps.  The partial sums (M x N floats
+  // per split) are small next to the weights at these row counts.  Taken
+  // where it measured faster on MI355X: waves with at least 8 steps (1B
+  // down at M <= 16: 11.6-14.9 -> 9.7-11.2 us; 8B down at M <= 4: 16.4-18.3
+  // -> 14.3-15.2 us) or at least 16 rows (8B q at M = 16: 11.1 -> 9.9 us);
+  // with 4 steps per wave and fewer rows the reduce launch costs more than
+  // the parallelism gains (8B q at M <= 8: +0.4-0.9 us).
+  const bool deep = (sps + wk - 1) / wk >= 8 || pl.mrows >= 16;
+  int64_t sps2 = sps, split2 = split;
+  while (deep && blocks * split2 * pl.mz < 256 && sps2 >= 4 * wk) {
+    split2 *= 2;
+    sps2 = (steps + split2 - 1) / split2;
+  }
+  const int64_t sps_final = sps2;
+  pl.split = (int)((steps + sps_final - 1) / sps_final);
+  pl.k_slice = sps_final * SK_STEP;
   pl.wk = wk;
   pl.wn = SK_W / wk;
-  pl.spw = (int)((sps + wk - 1) / wk);
-  pl.blocks = (ncb + pl.wn - 1) / pl.wn;
-  pl.x_lds = (int)(sps * per_step);
+  pl.spw = (int)((sps_final + wk - 1) / wk);
+  pl.blocks = blocks;
+  pl.x_lds = (int)(sps_final * per_step);
   pl.red_lds = wk > 1 ? (int)red : 0;
   const int64_t lds = pl.x_lds + pl.red_lds;
   const int64_t occ = lds * 2 <= kLds ? 2 : 1;  // workgroups per CU
-  int64_t grid = 256 * occ / split / pl.mz;  // workgroups per row block
+  int64_t grid = 256 * occ / pl.split / pl.mz;  // workgroups per row block
   if (grid < 1) grid = 1;
   if (grid > pl.blocks) grid = pl.blocks;
   pl.grid = (int)(grid * pl.mz);

@@ -8,7 +8,9 @@ beside each case):
     the latter with several column blocks per persistent workgroup;
   * a K whose last 128-k step is partial (K % 128 != 0);
   * K split across workgroups when one row block's binary16 activations
-    exceed LDS (M = 16 and M = 32 at K = 8192), with the split-K reduce;
+    exceed LDS (M = 16 and M = 32 at K = 8192), or when narrow N leaves CUs
+    without a block (the down projections at few rows), with the split-K
+    reduce;
   * staging of the activations in several rounds (M * K / 8 > 2048);
   * more than 32 rows: row blocks of 32 in separate workgroups;
   * ragged N, both nibble orders, per-channel and grouped scales (32, 128),
@@ -75,7 +77,10 @@ def test_two_row_blocks(M, K, N, gs, expect):
     (32, 2048, 256, 32, "activations staged in four rounds"),
     (16, 8192, 300, 32, "K split over 2 workgroups + reduce"),
     (32, 8192, 520, 128, "K split over 4 workgroups + reduce, 160 KiB of LDS"),
-    (4, 8192, 2048, 32, "the 1B down projection at M=4, one slice"),
+    (4, 8192, 2048, 32, "the 1B down projection at M=4: K split over 4 workgroups for parallelism"),
+    (2, 14336, 4096, 128, "the 8B down projection at M=2: K split over 2 for parallelism"),
+    (16, 4096, 4096, 128, "16 rows, 4 steps a wave: K split over 2 for parallelism"),
+    (8, 4096, 4096, 128, "8 rows, 4 steps a wave: one slice"),
     (7, 2048, 8192, 0, "the 1B gate projection, per-channel"),
     (1, 4096, 777, 32, "one row"),
     (12, 128, 33, 32, "the smallest K"),
