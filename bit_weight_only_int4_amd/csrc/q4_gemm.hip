@@ -25,14 +25,16 @@
 //  * Inside every 8-element group the k order follows the nibble order of
 //    the packed word (pairs (i, i+4)); the activations are stored with the
 //    same permutation, so A and B fragments pair up k for k.
-//  * Two kernels.  The pipelined one (aligned rows, K % 32 == 0, power-of-
-//    two groups >= 32 or per-channel scales) streams every operand into an
-//    LDS ring with buffer loads that write LDS directly, and unpacks each
-//    weight word once, in registers, into MFMA operands (details at the
-//    kernel).  The general one takes every other shape: any group size,
-//    unaligned rows, ragged K; it stages binary16 weight tiles in LDS from a
-//    register ring of global loads and masks the edges (0x88 bytes past the
-//    end of a row, predicated stores).  No fall-back kernel beyond these.
+//  * Two kernels.  The pipelined one (aligned rows, even K, power-of-two
+//    groups >= 32 or per-channel scales) streams every operand into an LDS
+//    ring with buffer loads that write LDS directly, and unpacks each weight
+//    word once, in registers, into MFMA operands (details at the kernel);
+//    when K is not a multiple of the 64-k step, the pre-pass also copies
+//    each row's bytes of the last step (bytes past K as 0x88) and the
+//    kernel reads that step from the copy.  The general one takes every
+//    other shape: any group size, unaligned rows, odd K; it stages binary16
+//    weight tiles in LDS from a register ring of global loads and masks the
+//    edges (0x88 bytes past the end of a row, predicated stores).
 //  * Scales come as fp32 or as binary16 (q4f16_1 weights); a binary16
 //    scale is its own RN16, so both give the same operands.
 //  * Split-K (grid.z > 1), only for deep K on few tiles, writes fp32
@@ -84,10 +86,39 @@ __device__ __forceinline__ void tile_of(uint32_t tile, int tiles_m, int tiles_n,
 // group of 8 the k' follow the nibble order of the packed words (pairs
 // (i, i + 4)); rows >= M and k >= K are zero.  A thread converts 8
 // elements; a workgroup covers 2048 k of a row, grid.y strides the rows.
+// With qtail (K % 64 != 0, the pipelined kernel) the threads also copy, for
+// every weight row n < N, the 32 bytes of its last 64-k step into qtail[n],
+// bytes past the row's K / 2 replaced by 0x88 (codes 8, c = 0): the
+// pipelined kernel reads that step from there, so no 16-byte piece of it
+// extends past a row.
 template <int ORDER>
 __global__ void __launch_bounds__(256)
 x16_kernel(const float* __restrict__ x, int64_t ldx, int64_t M, int64_t K,
-           _Float16* __restrict__ x16, int64_t mp, int64_t kp) {
+           _Float16* __restrict__ x16, int64_t mp, int64_t kp,
+           const uint8_t* __restrict__ qw, int64_t ldq, int64_t N,
+           uint8_t* __restrict__ qtail) {
+  if (qtail) {
+    const int64_t kbyte = ((K - 1) / 64) * 32;  // first byte of the last step
+    const int64_t rowb = K / 2;                  // bytes of a row (K even)
+    const int64_t t = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t nt = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    for (int64_t n = t; n < N; n += nt) {
+      uint32_t w[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int64_t o = kbyte + 4 * d + b;
+          v |= (uint32_t)(o < rowb ? qw[n * ldq + o] : 0x88u) << (8 * b);
+        }
+        w[d] = v;
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(qtail + n * 32);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) dst[d] = w[d];
+    }
+  }
   const int64_t k0 = (int64_t)blockIdx.x * 2048 + 8 * threadIdx.x;
   if (k0 >= kp) return;
   for (int64_t r = blockIdx.y; r < mp; r += gridDim.y) {
@@ -366,8 +397,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // ---------------------------------------------------------------------------
 // Pipelined fast path: power-of-two group sizes >= 32 or per-channel
-// scales, K a multiple of 32, dword-aligned weight rows, every byte offset
-// below 2^32; 128 x 128 tiles.
+// scales, even K, dword-aligned weight rows, every byte offset below 2^32;
+// 128 x 128 tiles.  With K % 64 != 0 the last step's weights come from the
+// pre-pass's 32-byte copy of each row (bytes past K as 0x88).
 // Global memory reaches LDS by buffer loads that write LDS directly, so no
 // registers hold data in flight and up to NSTAGE steps of activations,
 // packed weights and scales are in flight at once: the workgroup waits for
@@ -493,6 +525,10 @@ gemm_pipe_kernel(const GemmParams p) {
       make_rsrc(uniform_ptr(p.x16 + m0 * p.x16_pitch), (uint64_t)BM * p.x16_pitch * 2);
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(p.qw, (uint64_t)(p.N - 1) * p.ldq + (uint64_t)((p.K + 1) >> 1));
+  // the last 64-k step's weights from the pre-pass's copy when K % 64 != 0
+  // (kb_tail never matches a step otherwise)
+  const __amdgpu_buffer_rsrc_t rqt = make_rsrc(p.qtail, p.qtail ? (uint64_t)p.N * 32 : 0);
+  const uint32_t kb_tail = p.qtail ? (uint32_t)(((p.K - 1) / KS) * KS) : 0xFFFFFFFFu;
   constexpr uint32_t SB = S16 ? 2 : 4;  // bytes per scale
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(S16 ? (const void*)p.scales16 : (const void*)p.scales,
@@ -510,10 +546,11 @@ gemm_pipe_kernel(const GemmParams p) {
   // 16-byte half lane & 1.  The arrays have a fixed bound (NI <= 2): with a
   // bound taken from the template arguments, the lambda below that captures
   // them leaves the kernel without its host-side launch stub.
-  uint32_t vq[2], vs[2];
+  uint32_t vq[2], vs[2], vt[2];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
     vq[u] = (uint32_t)((n0 + c0 + 32 * u + (lane >> 1)) * p.ldq + 16 * (lane & 1));
+    vt[u] = (uint32_t)((n0 + c0 + 32 * u + (lane >> 1)) * 32 + 16 * (lane & 1));
     // scales of block u: lane -> half lb's group, column c0 + 32u + li
     vs[u] = (uint32_t)(((n0 + c0 + 32 * u + li) & (S16 ? ~1 : ~0)) * SB);
   }
@@ -526,10 +563,12 @@ gemm_pipe_kernel(const GemmParams p) {
     for (int u = 0; u < 4; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_ptr_t)((char*)&sm.a[st][0] + (w * 4 + u) * 1024), 16, va[u] + 2 * kb, 0, 0, 0);
+    const bool tail = kb == kb_tail;
 #pragma unroll
     for (int u = 0; u < NI; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, (lds_ptr_t)((char*)&sm.q[st][0] + (w * NI + u) * 1024), 16, vq[u] + (kb >> 1), 0, 0, 0);
+          tail ? rqt : rq, (lds_ptr_t)((char*)&sm.q[st][0] + (w * NI + u) * 1024), 16,
+          tail ? vt[u] : vq[u] + (kb >> 1), 0, 0, 0);
     if (!PERCH)
 #pragma unroll
       for (int u = 0; u < NI; ++u)
@@ -797,7 +836,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t group_size) {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   const GemmPlan pl = plan_gemm(M, N, K, group_size);
   size_t b = align256((size_t)pl.x16_rows * (size_t)pl.x16_pitch * sizeof(_Float16));
-  if (pl.split > 1) b += (size_t)pl.split * (size_t)M * (size_t)N * sizeof(float);
+  if (pl.split > 1) b += align256((size_t)pl.split * (size_t)M * (size_t)N * sizeof(float));
+  if (K % KS != 0) b += (size_t)N * 32;  // the last step's weights (pipelined kernel)
   const size_t sk = skinny_workspace_bytes(M, N, K, group_size);
   return b > sk ? b : sk;
 }
@@ -817,8 +857,9 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
   p.x16_pitch = pl.x16_pitch;
   char* ws = reinterpret_cast<char*>(workspace);
   p.x16 = reinterpret_cast<_Float16*>(ws);
-  p.partial = reinterpret_cast<float*>(
-      ws + align256((size_t)pl.x16_rows * (size_t)pl.x16_pitch * sizeof(_Float16)));
+  const size_t x16_bytes = align256((size_t)pl.x16_rows * (size_t)pl.x16_pitch * sizeof(_Float16));
+  p.partial = reinterpret_cast<float*>(ws + x16_bytes);
+  p.qtail = nullptr;
   int smode;
   if (p.group_size == 0 || p.group_size >= p.K) {
     smode = kPerChannel;
@@ -836,24 +877,14 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
     while ((1LL << l2) < p.group_size) ++l2;
     p.log2_gs = l2;
   }
-  // 1. activations to binary16 (RN16), permuted and zero-padded
-  const dim3 xgrid((unsigned)((pl.x16_pitch + 2047) / 2048),
-                   (unsigned)(pl.x16_rows < 65535 ? pl.x16_rows : 65535));
-  if (order == 0)
-    hipLaunchKernelGGL(x16_kernel<0>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
-                       pl.x16_rows, pl.x16_pitch);
-  else
-    hipLaunchKernelGGL(x16_kernel<1>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
-                       pl.x16_rows, pl.x16_pitch);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // 2. the GEMM
-  // the branch-free kernel: power-of-two groups >= 32 or per-channel,
-  // dword-aligned rows, K a multiple of 32 (each 16-byte weight chunk lies
-  // wholly inside a row or wholly past its end: a vector load that crosses
-  // the end of its resource returns zeros for all of its bytes), and all
-  // byte offsets of its buffers below 2^32
-  const bool pow2 = smode == kGroup32 && p.log2_gs >= 5 && p.K % 32 == 0;
+  // The branch-free kernel: power-of-two groups >= 32 or per-channel,
+  // dword-aligned rows, even K, and all byte offsets of its buffers below
+  // 2^32.  Every 16-byte weight piece of its steps lies inside a row except
+  // in the last 64-k step when K % 64 != 0 (a vector load that crosses the
+  // end of its resource returns zeros for all of its bytes, and one inside
+  // another row's bytes would bring codes that need not be 8): that step is
+  // read from the pre-pass's copy, whose bytes past K are 0x88.
+  const bool pow2 = smode == kGroup32 && p.log2_gs >= 5;
   const bool small = (uint64_t)p.N * (uint64_t)p.ldq < (1ull << 32) &&
                      (uint64_t)p.G * (uint64_t)p.lds * 4 < (1ull << 32) &&
                      (uint64_t)pl.x16_rows * (uint64_t)pl.x16_pitch * 2 < (1ull << 32);
@@ -862,7 +893,25 @@ hipError_t launch_gemm(const GemmParams& p0, int order, bool qa4, void* workspac
   const bool s16ok = !p.scales16 || smode == kPerChannel ||
                      (p.N % 2 == 0 && p.lds % 2 == 0 &&
                       reinterpret_cast<uintptr_t>(p.scales16) % 4 == 0);
-  if (qa4 && small && s16ok && p.K % 32 == 0 && (smode == kPerChannel || pow2)) {
+  const bool pipe = qa4 && small && s16ok && p.K % 2 == 0 && (smode == kPerChannel || pow2);
+  if (pipe && p.K % KS != 0)
+    p.qtail = reinterpret_cast<uint8_t*>(ws) + x16_bytes +
+              (pl.split > 1 ? align256((size_t)pl.split * (size_t)p.M * (size_t)p.N * sizeof(float))
+                            : 0);
+  // 1. activations to binary16 (RN16), permuted and zero-padded; the last
+  // step's weights for the pipelined kernel when K % 64 != 0
+  const dim3 xgrid((unsigned)((pl.x16_pitch + 2047) / 2048),
+                   (unsigned)(pl.x16_rows < 65535 ? pl.x16_rows : 65535));
+  if (order == 0)
+    hipLaunchKernelGGL(x16_kernel<0>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
+                       pl.x16_rows, pl.x16_pitch, p.qw, p.ldq, p.N, p.qtail);
+  else
+    hipLaunchKernelGGL(x16_kernel<1>, xgrid, dim3(256), 0, s, p.x, p.ldx, p.M, p.K, p.x16,
+                       pl.x16_rows, pl.x16_pitch, p.qw, p.ldq, p.N, p.qtail);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 2. the GEMM
+  if (pipe) {
     const bool wide = pipe_wide(pl);
     if (wide) p.tiles_n = (int)((p.N + 255) / 256);
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), 1, (unsigned)pl.split);

@@ -97,6 +97,10 @@ struct GemmParams {
   float* partial;      // split-K workspace [split][M][N] (split > 1)
   _Float16* x16;       // binary16 activations [x16_rows][x16_pitch] (workspace)
   int64_t x16_pitch;
+  // pipelined kernel with K % 64 != 0: each row's bytes of the last 64-k step
+  // (32 per row, bytes past K as 0x88), written by the binary16 pre-pass into
+  // the workspace; else nullptr
+  uint8_t* qtail;
   int32_t log2_gs;     // group index by shift (power-of-two group size), else -1
   int64_t M, N, K;
   int64_t k_per_split; // multiple of the K step, filled by launch_gemm

@@ -102,9 +102,11 @@ typedef int32_t q4_status;
                                      few-row kernel (M <= 32, and M <= 64 when
                                      N * K <= 2^25 or N >= 65536; K % 32 == 0,
                                      per-channel or power-of-two groups >= 32,
-                                     dword-aligned weight rows): one launch
-                                     unless a row block's binary16 activations
-                                     exceed LDS */
+                                     dword-aligned weight rows): one launch,
+                                     plus the split-K reduce where a row
+                                     block's binary16 activations exceed LDS
+                                     or narrow N over deep K leaves CUs
+                                     without a workgroup */
 
 /* Element type of q4_dequant's output. */
 #define Q4_DTYPE_F32 0

@@ -157,7 +157,47 @@ def test_row_pitches_and_unaligned_rows(math):
 
 
 # ---- the pipelined GEMM's output stores ----------------------------------
-# The pipelined kernel (dword-aligned weight rows, K % 32 == 0, power-of-two
+# ---- the pipelined GEMM when K is not a multiple of its 64-k step ----------
+# The binary16 pre-pass also copies each weight row's bytes of the last step
+# (bytes past K as 0x88) and the kernel reads that step from the copy: even
+# K of every remainder, rows of K / 2 bytes (K % 8 == 0) and padded to a
+# dword, partial last groups, split K, 128 x 256 tiles.
+@pytest.mark.parametrize("M,K,N,gs,qpad,order", [
+    (65, 2008, 3000, 0, 0, "high_first"),    # the 2008 x 3000 workload: K % 64 = 24
+    (100, 1000, 520, 32, 0, "low_first"),    # K % 64 = 40, a last group of 8
+    (200, 2040, 300, 128, 0, "high_first"),  # a last group of 120
+    (130, 200, 3000, 0, 0, "low_first"),     # K % 64 = 8
+    (96, 2010, 256, 32, 3, "low_first"),     # K % 8 = 2: rows of 1005 bytes padded to 1008
+    (128, 8200, 256, 32, 0, "high_first"),   # split K, the last step in the last split
+    (136, 264, 16400, 32, 0, "low_first"),   # 128 x 256 tiles
+])
+def test_pipelined_gemm_k_tail(M, K, N, gs, qpad, order):
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=True, seed=M + K)
+    check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16", pad=(0, qpad, 0, 0),
+               label="pipe-ktail")
+
+
+def test_pipelined_gemm_bytes_past_k_do_not_reach_the_sum():
+    """Row bytes past K (the pitch's 0xFF padding: code 15) under scales of
+    30000 would dequantize to inf in binary16, and inf * 0 = NaN; the last
+    step's copy holds 0x88 there, so the result stays finite."""
+    need_gpu()
+    rng = np.random.default_rng(8)
+    M, K, N = 70, 2008, 300
+    raw = rng.integers(7, 10, size=(N, K))  # c in {-1, 0, 1}: |c * s| <= 30000
+    qw = torch.from_numpy(pack(raw, "low_first"))
+    x = torch.from_numpy(rng.uniform(-1, 1, size=(M, K)).astype(np.float32))
+    s = torch.full((N,), 30000.0)
+    out, path, guards = run_gpu(x, qw, s, None, K=K, gs=0, order="low_first", math="f16",
+                                pad=(0, 48, 0, 0))
+    ref, den = oracle_full(x, qw, s, None, K=K, gs=0, order="low_first")
+    assert path == "gemm_f16" and guards
+    assert np.all(np.isfinite(out))
+    assert normalised_error(out, ref, den) <= 2e-3
+
+
+# The pipelined kernel (dword-aligned weight rows, even K, power-of-two
 # groups >= 32 or per-channel) stores 16-byte row segments when the output
 # rows allow it and element by element otherwise; split-K partials likewise.
 # These shapes hit every branch: an output pitch that is not a multiple of 4,
