@@ -58,6 +58,38 @@ __global__ void __launch_bounds__(256)
 requant_kernel(const float* __restrict__ latent, int64_t ldl, const float* __restrict__ scales,
                int64_t lds, int64_t gs, int log2_gs, int64_t N, int64_t K,
                uint8_t* __restrict__ qw, int64_t ldq) {
+  // Blocks of 2048 k wholly inside K, 16-byte aligned latents, groups of a
+  // multiple of 4 k and 2-byte aligned code rows: thread t rounds the 4 k at
+  // 4t and at 1024 + 4t of the block, so each wave-wide 16-byte load reads
+  // 1 KiB of one row, and writes their codes as two 2-byte pieces.
+  const int64_t kbl = (int64_t)blockIdx.x * 2048;
+  if (kbl + 2048 <= K && (ldl % 4) == 0 && (reinterpret_cast<uintptr_t>(latent) % 16) == 0 &&
+      (gs == 0 || gs % 4 == 0) && (ldq % 2) == 0 && (reinterpret_cast<uintptr_t>(qw) % 2) == 0) {
+    for (int64_t n = blockIdx.y; n < N; n += gridDim.y) {
+      const float* lrow = latent + n * ldl;
+      uint8_t* qrow = qw + n * ldq;
+      f4 a[2];
+      float sc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t k = kbl + 1024 * h + 4 * threadIdx.x;
+        a[h] = *reinterpret_cast<const f4*>(lrow + k);
+        int64_t srow = 0;
+        if (gs > 0) srow = log2_gs >= 0 ? (k >> log2_gs) : (int64_t)((uint64_t)k / (uint64_t)gs);
+        sc[h] = scales[srow * lds + n];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t c0 = requant_code(a[h].x, sc[h]), c1 = requant_code(a[h].y, sc[h]);
+        const uint32_t c2 = requant_code(a[h].z, sc[h]), c3 = requant_code(a[h].w, sc[h]);
+        const uint32_t b0 = ORDER == kLowFirst ? (c0 | (c1 << 4)) : (c1 | (c0 << 4));
+        const uint32_t b1 = ORDER == kLowFirst ? (c2 | (c3 << 4)) : (c3 | (c2 << 4));
+        const int64_t k = kbl + 1024 * h + 4 * threadIdx.x;
+        *reinterpret_cast<uint16_t*>(qrow + k / 2) = (uint16_t)(b0 | (b1 << 8));
+      }
+    }
+    return;
+  }
   const int64_t wd = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t Kp = (K + 1) >> 1;
   if (4 * wd >= Kp) return;
