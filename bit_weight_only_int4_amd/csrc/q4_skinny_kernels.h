@@ -201,14 +201,19 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
     }
   };
 
-  // 1. The activations of the slice, RN16, into LDS.  16-byte slot of
-  //    (step s, MFMA t, lane group g, row m): ((s * 4 + t) * 4 + g) * M + m;
-  //    it holds k = kz0 + 128 s + 32 g + 8 t + (0..7) in nibble order, zeros
-  //    past K.  A thread converts four 8-k chunks per round, their loads
-  //    issued together (no branch around them: a chunk past K or past the
-  //    last one reads the row start and is zeroed, or repeats the last chunk).  The ring's
-  //    first D steps go out between the last round's loads and their use, so
-  //    that the two latencies overlap.
+  // 1. The activations of the slice, RN16, into LDS.  16-byte slot of row
+  //    m, chunk c: m * cpr + (c ^ (m & 15)); it holds k = kz0 + 8 c + (0..7)
+  //    in nibble order, zeros past K.  MFMA t of step s reads chunk
+  //    16 s + 4 g + t for lane group g.  The XOR keeps a chunk inside its
+  //    aligned group of 16 and spreads both a wave's staging stores
+  //    (consecutive chunks of one row) and its operand reads (16 rows of one
+  //    chunk per lane group) over 16 different groups of four banks; rows
+  //    cpr slots apart without it (cpr a multiple of 16) put every store of a
+  //    wave on the same four banks.  A thread converts four 8-k chunks per
+  //    round, their loads issued together (no branch around them: a chunk
+  //    past K or past the last one reads the row start and is zeroed, or
+  //    repeats the last chunk).  The ring's first D steps go out between the
+  //    last round's loads and their use, so that the two latencies overlap.
   const int cpr = sps * 16;  // 8-k chunks per row
   const int total = M * cpr;
   const __amdgpu_buffer_rsrc_t rxa =
@@ -243,10 +248,9 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
       h8 h;
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) h[sl] = (_Float16)f[pair_k<ORDER>(sl >> 1, sl & 1)];
-      const int s = st.k[u] >> 4, gg = (st.k[u] >> 2) & 3, t = st.k[u] & 3;
       // (a chunk past the last one repeats the last one: the same bytes to
       // the same slot)
-      *reinterpret_cast<h8*>(xs + (((s * 4 + t) * 4 + gg) * M + st.m[u]) * 16) = h;
+      *reinterpret_cast<h8*>(xs + (st.m[u] * cpr + (st.k[u] ^ (st.m[u] & 15))) * 16) = h;
     }
   };
   const int rounds = (total + 4 * NT - 1) / (4 * NT);
@@ -281,22 +285,22 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
 
   // A operands: lane (row m, group g).  Rows m >= M read row M - 1: an
   // output row depends on its own A row only, and rows >= M are never stored.
-  int aoff[MB];
+  int aoff[MB][4];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = li + 16 * mb < M ? li + 16 * mb : M - 1;
-    aoff[mb] = (g * M + m) * 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aoff[mb][t] = (m * cpr + ((4 * g + t) ^ (m & 15))) * 16;
   }
-  const int tstride = 4 * M * 16;  // bytes between the MFMA slots of one step
 
   auto compute = [&](const SkSlot<NI>& sl, int sidx) {
-    const char* ab = xs + sidx * 4 * tstride;
+    const char* ab = xs + sidx * 256;  // chunk 16 sidx of row 0
     h8 a[4][MB];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        a[t][mb] = *reinterpret_cast<const h8*>(ab + t * tstride + aoff[mb]);
+        a[t][mb] = *reinterpret_cast<const h8*>(ab + aoff[mb][t]);
     if constexpr (SC == SC_ELEM) {
       // chunks past K (the last step of a K that is not a multiple of 128)
       // get a zero scale, so that whatever bytes they read give w = 0
