@@ -1,4 +1,4 @@
-// q4_skinny_kernels.h -- MFMA GEMM for few activation rows (1 <= M <= 64) on
+// q4_skinny_kernels.h -- MFMA GEMM for few activation rows (1 <= M <= 96) on
 // gfx950: binary16 operands, fp32 accumulation, the arithmetic of the tiled
 // prefill GEMM (q4_gemm.hip):
 //
@@ -303,7 +303,9 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
         a[t][mb] = *reinterpret_cast<const h8*>(ab + aoff[mb][t]);
     if constexpr (SC == SC_ELEM) {
       // chunks past K (the last step of a K that is not a multiple of 128)
-      // get a zero scale, so that whatever bytes they read give w = 0
+      // get a zero scale, so that whatever bytes they read give w = 0 (the
+      // plan takes this mode only with K % 32 == 0: a lane's 32-k chunk lies
+      // wholly inside K or wholly past it)
       const bool pastk = kz0 + SK_STEP * sidx + 32 * g >= K;
       h2 s16[NI];
 #pragma unroll
@@ -323,7 +325,10 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
             acc[u][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][mb], bv, acc[u][mb], 0, 0, 0);
         }
     } else {
-      // B = c exactly (chunks past K meet zero activations: c is finite)
+      // B = c exactly: chunks past K, and with K % 32 != 0 the 8-k words
+      // past K of the chunk that straddles it (bytes of the row pitch, of the
+      // next row, or zeros past the array), meet activations staged as zero,
+      // and c is finite, so they add exactly 0
       f4 st[NI][MB];
 #pragma unroll
       for (int u = 0; u < NI; ++u)

@@ -99,10 +99,13 @@ typedef int32_t q4_status;
 #define Q4_PATH_BWD_F32 3   /* fp32 input gradient (q4_linear_backward) */
 #define Q4_PATH_BWD_F16 4   /* MFMA f16 x f16 -> f32 input gradient */
 #define Q4_PATH_GEMM_F16_SKINNY 5 /* binary16 operands, fp32 sums, from the
-                                     few-row kernel (M <= 32, and M <= 64 when
-                                     N * K <= 2^25 or N >= 65536; K % 32 == 0,
-                                     per-channel or power-of-two groups >= 32,
-                                     dword-aligned weight rows): one launch,
+                                     few-row kernel (M <= 32; M <= 64 when
+                                     N * K <= 2^25 or N >= 65536; M <= 96 when
+                                     N * K <= 2^24 and N <= 4096; K % 32 == 0,
+                                     or K % 8 == 0 with per-channel scales or
+                                     groups >= 128; per-channel or power-of-two
+                                     groups >= 32, dword-aligned weight rows):
+                                     one launch,
                                      plus the split-K reduce where a row
                                      block's binary16 activations exceed LDS
                                      or narrow N over deep K leaves CUs

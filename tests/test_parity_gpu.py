@@ -130,7 +130,9 @@ def test_gemm_shapes(M, K, N, gs, order):
     (4, 2048, 8192, 32, "gemm_f16_skinny"), (8, 2048, 8192, 32, "gemm_f16_skinny"),
     (5, 2048, 2048, 32, "gemm_f16_skinny"), (16, 2048, 2048, 32, "gemm_f16_skinny"),
     (32, 2048, 300, 0, "gemm_f16_skinny"), (33, 2048, 300, 0, "gemm_f16_skinny"),
-    (65, 2048, 300, 0, "gemm_f16"),
+    (65, 2048, 300, 0, "gemm_f16_skinny"), (96, 2048, 4096, 128, "gemm_f16_skinny"),
+    (97, 2048, 300, 0, "gemm_f16"), (80, 2048, 8192, 32, "gemm_f16"),
+    (65, 2008, 3000, 0, "gemm_f16_skinny"), (65, 2008, 3000, 32, "gemm_f16"),
     (2, 2048, 128257, 0, "gemm_f16_skinny"), (7, 2048, 128257, 0, "gemm_f16_skinny"),
     (2, 14336, 4096, 128, "gemm_f16_skinny"), (3, 4096, 14336, 128, "gemm_f16_skinny"),
     (4, 2048, 300, 8, "gemm_f16"), (4, 2040, 300, 32, "gemv_f32"),
@@ -163,7 +165,7 @@ def test_row_pitches_and_unaligned_rows(math):
 # K of every remainder, rows of K / 2 bytes (K % 8 == 0) and padded to a
 # dword, partial last groups, split K, 128 x 256 tiles.
 @pytest.mark.parametrize("M,K,N,gs,qpad,order", [
-    (65, 2008, 3000, 0, 0, "high_first"),    # the 2008 x 3000 workload: K % 64 = 24
+    (97, 2008, 3000, 0, 0, "high_first"),    # the 2008 x 3000 shape: K % 64 = 24
     (100, 1000, 520, 32, 0, "low_first"),    # K % 64 = 40, a last group of 8
     (200, 2040, 300, 128, 0, "high_first"),  # a last group of 120
     (130, 200, 3000, 0, 0, "low_first"),     # K % 64 = 8
@@ -174,8 +176,9 @@ def test_row_pitches_and_unaligned_rows(math):
 def test_pipelined_gemm_k_tail(M, K, N, gs, qpad, order):
     need_gpu()
     x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=True, seed=M + K)
-    check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16", pad=(0, qpad, 0, 0),
-               label="pipe-ktail")
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
+                            pad=(0, qpad, 0, 0), label="pipe-ktail")
+    assert path == "gemm_f16"
 
 
 def test_pipelined_gemm_bytes_past_k_do_not_reach_the_sum():
@@ -184,7 +187,7 @@ def test_pipelined_gemm_bytes_past_k_do_not_reach_the_sum():
     step's copy holds 0x88 there, so the result stays finite."""
     need_gpu()
     rng = np.random.default_rng(8)
-    M, K, N = 70, 2008, 300
+    M, K, N = 100, 2008, 300
     raw = rng.integers(7, 10, size=(N, K))  # c in {-1, 0, 1}: |c * s| <= 30000
     qw = torch.from_numpy(pack(raw, "low_first"))
     x = torch.from_numpy(rng.uniform(-1, 1, size=(M, K)).astype(np.float32))
@@ -206,15 +209,16 @@ def test_pipelined_gemm_bytes_past_k_do_not_reach_the_sum():
 @pytest.mark.parametrize("M,K,N,gs,pad_out", [
     (200, 512, 203, 32, 3),     # no split; element stores (output pitch 206)
     (130, 2048, 8202, 64, 2),   # no split; 16-byte stores, last quad ragged, M tail
-    (64, 8192, 130, 128, 0),    # split K; element stores of partials (N % 4 == 2)
-    (96, 4096, 264, 32, 0),     # split K; 16-byte stores of partials
+    (100, 8192, 130, 128, 0),   # split K; element stores of partials (N % 4 == 2)
+    (100, 4096, 264, 32, 0),    # split K; 16-byte stores of partials
     (333, 512, 516, 0, 0),      # per-channel scales; 16-byte stores, M tail
 ])
 def test_pipelined_gemm_output_stores(M, K, N, gs, pad_out):
     need_gpu()
     x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=M + K + N)
-    check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
-               pad=(0, 0, 0, pad_out), label="pipe-stores")
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
+                            pad=(0, 0, 0, pad_out), label="pipe-stores")
+    assert path == "gemm_f16"
 
 
 # ---- the pipelined GEMM's 128 x 256 tiles --------------------------------

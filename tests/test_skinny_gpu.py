@@ -1,4 +1,4 @@
-"""GPU parity of the few-row MFMA GEMM (M <= 64) against the fp64 oracle,
+"""GPU parity of the few-row MFMA GEMM (M <= 96) against the fp64 oracle,
 through the C ABI, and the boundary between it and the tiled GEMM.
 
 The kernel's plan depends on the sizes alone, so the shapes below are
@@ -6,13 +6,15 @@ chosen to reach each of its regimes (derived from the plan's rules, stated
 beside each case):
   * waves of a workgroup along K (wk = 8, 4, 2) and along N only (wk = 1),
     the latter with several column blocks per persistent workgroup;
-  * a K whose last 128-k step is partial (K % 128 != 0);
+  * a K whose last 128-k step is partial (K % 128 != 0), and K % 32 != 0
+    (whole 8-k chunks) where the scale is taken out of the sums;
   * K split across workgroups when one row block's binary16 activations
     exceed LDS (M = 16 and M = 32 at K = 8192), or when narrow N leaves CUs
     without a block (the down projections at few rows), with the split-K
     reduce;
   * staging of the activations in several rounds (M * K / 8 > 2048);
-  * more than 32 rows: row blocks of 32 in separate workgroups;
+  * more than 32 rows: row blocks of 32 in separate workgroups (two or
+    three);
   * ragged N, both nibble orders, per-channel and grouped scales (32, 128),
     fp32 and binary16 scales, bias on and off, row pitches, and a NaN-poisoned
     output with guard rows and columns.
@@ -37,19 +39,19 @@ def inputs(M, K, N, gs, order="low_first", bias=False, seed=0):
     return make_inputs(p, seed)
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 24, 32, 33, 48, 64, 65])
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 24, 32, 33, 48, 64, 65, 96, 97])
 @pytest.mark.parametrize("order", ["low_first", "high_first"])
 @pytest.mark.parametrize("gs", [0, 32, 128])
 def test_rows_around_the_boundary(M, order, gs):
-    """M <= 64 runs the skinny kernel here (N * K <= 2^25; above 32 rows in
-    two row blocks), M >= 65 the tiled GEMM; N = 1000 is ragged against 16-
-    and 32-column blocks (wk = 8 here)."""
+    """M <= 96 runs the skinny kernel here (N * K <= 2^24 and N <= 4096;
+    above 32 rows in row blocks of 32), M >= 97 the tiled GEMM; N = 1000 is
+    ragged against 16- and 32-column blocks (wk = 8 here)."""
     need_gpu()
     K, N = 2048, 1000
     x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 1), seed=M * 31 + gs)
     _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
                             label="skinny-boundary")
-    assert path == (SKINNY if M <= 64 else "gemm_f16")
+    assert path == (SKINNY if M <= 96 else "gemm_f16")
 
 
 @pytest.mark.parametrize("M,K,N,gs,expect", [
@@ -59,8 +61,13 @@ def test_rows_around_the_boundary(M, order, gs):
     (50, 2048, 70000, 0, SKINNY),            # vocabulary-sized N
     (64, 8192, 2048, 32, SKINNY),            # two row blocks, K split over 4 + reduce
     (41, 256, 3000, 32, SKINNY),             # two row blocks, the second of 9 rows
+    (65, 2048, 4096, 128, SKINNY),           # three row blocks, the third of 1 row
+    (90, 8192, 2048, 32, SKINNY),            # three row blocks, K split over 4 + reduce
+    (96, 4096, 4096, 0, SKINNY),             # N * K = 2^24, N = 4096
+    (70, 2048, 4097, 0, "gemm_f16"),         # N > 4096 above 64 rows: the tiled GEMM
+    (80, 4104, 4096, 0, "gemm_f16"),         # N * K > 2^24 above 64 rows
 ])
-def test_two_row_blocks(M, K, N, gs, expect):
+def test_row_blocks(M, K, N, gs, expect):
     need_gpu()
     x, qw, s, bias = inputs(M, K, N, gs, bias=True, seed=M + K + N)
     _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="high_first", math="f16",
@@ -114,15 +121,17 @@ def test_unaligned_weight_rows_take_the_tiled_kernel():
     assert path == "gemm_f16"
 
 
-@pytest.mark.parametrize("M,K,gs", [(8, 2056, 32), (8, 2048, 64), (8, 2048, 48), (8, 2048, 16)])
+@pytest.mark.parametrize("M,K,gs", [(8, 2056, 32), (8, 2056, 64), (8, 2048, 64), (8, 2048, 48),
+                                    (8, 2048, 16), (8, 2052, 0)])
 def test_other_shapes_take_the_tiled_kernel(M, K, gs):
-    """K % 32 != 0 and groups that are not powers of two >= 32 are the tiled
-    kernel's."""
+    """K % 32 != 0 with groups of 32 or 64 (the scale multiplies each
+    weight), K % 8 != 0, and groups that are not powers of two >= 32 are the
+    tiled kernel's."""
     need_gpu()
     x, qw, s, bias = inputs(M, K, 200, gs, seed=19)
     _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
                             label="skinny-other")
-    assert path == (SKINNY if gs == 64 else "gemm_f16")
+    assert path == (SKINNY if (gs == 64 and K % 32 == 0) else "gemm_f16")
 
 
 @pytest.mark.parametrize("M,gs", [(7, 0), (24, 32), (5, 128)])
@@ -206,3 +215,63 @@ def test_repeat_calls_are_bit_identical():
         c, pc, _ = run_gpu(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16")
         assert pa == pc == SKINNY
         assert np.array_equal(a, c)
+
+
+# ---- K % 32 != 0: whole 8-k chunks, the scale taken out of the sums -------
+# The last 16-byte weight chunk of a row then reaches past K: its bytes past
+# the row belong to the row pitch, the next row or (last row) lie past the
+# array, where the buffer load returns zeros.  They decode to finite codes
+# (B = c exactly, no scale in the operand) and meet activations that the
+# staging set to zero past K, so they add exactly nothing.
+@pytest.mark.parametrize("M,K,N,gs,order", [
+    (65, 2008, 3000, 0, "high_first"),   # the 2008 x 3000 workload, three row blocks
+    (7, 2008, 300, 128, "low_first"),    # a last group of 88
+    (33, 1000, 513, 0, "low_first"),     # K % 128 = 104, two row blocks
+    (5, 2056, 200, 0, "high_first"),     # K % 32 = 8
+    (96, 2040, 3000, 128, "low_first"),  # K % 32 = 24, three row blocks
+    (16, 8200, 300, 0, "high_first"),    # K split over workgroups, the straddle in the last slice
+    (3, 136, 70, 0, "low_first"),        # two steps, the second of 8 k
+])
+def test_k_not_a_multiple_of_32(M, K, N, gs, order):
+    need_gpu()
+    x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 1), seed=M + K + N)
+    _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
+                            label="skinny-k8")
+    assert path == SKINNY
+
+
+@pytest.mark.parametrize("M,gs", [(5, 0), (40, 128)])
+def test_k_not_a_multiple_of_32_bytes_past_k(M, gs):
+    """Row pitch padding of 0xFF (code 15) past K = 2008 and scales of 30000:
+    the straddling chunk's bytes past K still add nothing, and nothing turns
+    into inf or NaN."""
+    need_gpu()
+    rng = np.random.default_rng(11 + M)
+    K, N = 2008, 300
+    raw = rng.integers(7, 10, size=(N, K))
+    qw = torch.from_numpy(pack(raw, "low_first"))
+    x = torch.from_numpy(rng.uniform(-1, 1, size=(M, K)).astype(np.float32))
+    s = torch.full((N,) if gs == 0 else ((K + gs - 1) // gs, N), 30000.0)
+    out, path, guards = run_gpu(x, qw, s, None, K=K, gs=gs, order="low_first", math="f16",
+                                pad=(0, 48, 0, 0))
+    ref, den = oracle_full(x, qw, s, None, K=K, gs=gs, order="low_first")
+    assert path == SKINNY and guards
+    assert np.all(np.isfinite(out))
+    assert normalised_error(out, ref, den) <= 2e-3
+
+
+@pytest.mark.parametrize("M", [1, 33, 65])
+def test_k_not_a_multiple_of_32_integer_case_is_exact(M):
+    """x in {-2..2}, per-channel scales 2^-6, K = 2008: exact operands and
+    partial sums, so the kernel equals the oracle bit for bit."""
+    need_gpu()
+    rng = np.random.default_rng(200 + M)
+    K, N = 2008, 301
+    raw = rng.integers(0, 16, size=(N, K))
+    x = torch.from_numpy(rng.integers(-2, 3, size=(M, K)).astype(np.float32))
+    qw = torch.from_numpy(pack(raw, "high_first"))
+    s = torch.full((N,), 2.0 ** -6)
+    out, path, guards = run_gpu(x, qw, s, None, K=K, gs=0, order="high_first", math="f16")
+    ref, _ = oracle_full(x, qw, s, None, K=K, gs=0, order="high_first")
+    assert path == SKINNY and guards
+    assert np.array_equal(out.astype(np.float64), ref)
