@@ -331,6 +331,50 @@ def test_results_are_deterministic():
         assert np.array_equal(a, c)
 
 
+# Split K in the pipelined GEMM: the splits' fp32 partials go through the
+# workspace and the reduce kernel adds them in split order, then the bias.
+# Repeated calls and graph replays (three kernels per call) must give the
+# same bits, within the oracle's bound.
+@pytest.mark.parametrize("M,K,N,gs,bias", [
+    (512, 2048, 2048, 32, True),    # 64 tiles, 4 splits
+    (512, 8192, 2048, 32, False),   # 64 tiles, 4 splits of 32 steps
+    (100, 8192, 130, 128, True),    # 2 tiles, 16 splits, N % 4 != 0 (element path)
+    (200, 4096, 600, 0, True),      # 10 tiles, 8 splits, ragged M and N
+])
+def test_pipelined_split_k_repeats_and_replays(M, K, N, gs, bias):
+    need_gpu()
+    x, qw, s, bv = inputs(M, K, N, gs, bias=bias, seed=M + N)
+    dev = torch.device("cuda")
+    xd, qd, sd = x.to(dev), qw.to(dev), s.to(dev)
+    bd = bv.to(dev) if bias else None
+    first, path = b.linear(xd, qd, sd, bd, K=K, group_size=gs, math="f16", return_path=True)
+    torch.cuda.synchronize()
+    assert path == "gemm_f16"
+    ref, den = oracle_full(x, qw, s, bv if bias else None, K=K, gs=gs, order="low_first")
+    assert normalised_error(first.cpu().numpy(), ref, den) <= 2e-3
+    for _ in range(20):
+        again = b.linear(xd, qd, sd, bd, K=K, group_size=gs, math="f16")
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int32), first.view(torch.int32))
+    out = torch.empty(M, N, device=dev)
+    ws = torch.empty(b.workspace_bytes(M, N, K, gs, "f16"), dtype=torch.uint8, device=dev)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        b.linear(xd, qd, sd, bd, K=K, group_size=gs, math="f16", out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        b.linear(xd, qd, sd, bd, K=K, group_size=gs, math="f16", out=out, workspace=ws)
+    for _ in range(5):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), first.view(torch.int32))
+
+
 def test_split_k_gemv_with_large_k():
     """K beyond one workgroup's cover forces the split-K plan and its
     reduce kernel."""
