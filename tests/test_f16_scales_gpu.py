@@ -76,8 +76,10 @@ def _case(M, K, N, gs, *, order="low_first", math="auto", pad=(0, 0, 0, 0), bias
     # general GEMM: odd N, odd scale pitch, ragged K, small groups
     (97, 2048, 257, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
     (97, 2048, 300, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16"),
-    # few-row GEMM over three row blocks
+    # few-row GEMM over three row blocks, and K % 32 != 0 with factored scales
     (65, 2048, 300, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16_skinny"),
+    (65, 2008, 3000, 0, "high_first", "auto", (0, 0, 0, 0), "gemm_f16_skinny"),
+    (7, 2008, 300, 128, "low_first", "f16", (0, 0, 2, 0), "gemm_f16_skinny"),
     (40, 2007, 300, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
     (17, 300, 77, 8, "high_first", "f16", (0, 0, 0, 0), "gemm_f16"),
     (513, 1024, 260, 100, "low_first", "auto", (0, 0, 0, 0), "gemm_f16"),
