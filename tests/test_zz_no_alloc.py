@@ -26,6 +26,8 @@ PAIRS = [
     ((1, 20480, 512, 32, "low_first"), (1, 18432, 200, 64, "low_first")),
     ((4, 8192, 1024, 32, "low_first"), (3, 8192, 130, 0, "high_first")),
     ((1, 2048, 1024, 32, "low_first"), (1, 2048, 96, 0, "high_first")),
+    # few-row kernel over three row blocks with K split for LDS, then K % 32 != 0
+    ((90, 8192, 2048, 32, "low_first"), (65, 2008, 3000, 0, "high_first")),
 ]
 
 
