@@ -1,4 +1,4 @@
-// q4_skinny.hip -- the plan of the few-row MFMA GEMM (1 <= M <= 96) and its
+// q4_skinny.hip -- the plan of the few-row MFMA GEMM (1 <= M <= 256) and its
 // launch; the kernel and its design are in q4_skinny_kernels.h.
 #include "q4_kernels.h"
 
@@ -20,15 +20,19 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   // M = 64 on the Llama-3.2-1B projections (N * K <= 2^24: 11.0-17.4 us
   // against 13.7-21.9), the 8B q projection (16.3 against 20.4) and the
   // vocabulary-sized output head (71.6 against 83.5), not on the 8B gate/up
-  // and down projections (31.4 and 32.4 against 27.9 and 29.4); at
-  // M = 65-96 (three row blocks) on narrow N, where the tiled GEMM has few
-  // tiles and splits K (2048 x 2048: 9.4-9.9 against 14.7-15.4 us;
-  // 2008 x 3000: 11.8-12.3 against 17.3-18.7; 4096 x 4096: 18.8-19.8
-  // against 20.6-23.3; 8192 x 2048: 20.4-21.8 against 21.5-22.7), not on
-  // 2048 x 8192 (17.7-18.2 against 15.9-17.4).
+  // and down projections (31.4 and 32.4 against 27.9 and 29.4); on narrow
+  // N, where the tiled GEMM has few tiles and splits K: at M = 65-128 with
+  // N * K <= 2^24 (2048 x 2048: 9.4-10.1 against 14.7-16.4 us; 2008 x 3000:
+  // 11.8-12.5 against 17.3-19.9; 4096 x 4096: 18.8-21.7 against 20.6-26.0;
+  // 8192 x 2048: 20.4-23.0 against 21.5-26.1), not on 2048 x 8192
+  // (17.7-18.2 against 15.9-17.4 at M = 65-96); at M = 129-256 with
+  // N * K <= 2^23 (2048 x 2048: 12.7-12.9 against 17.7-19.7; 2008 x 3000:
+  // 12.7-14.9 against 21.5-24.6; 1024 x 1024: 7.4-7.7 against 14.0-14.4),
+  // not at 2^24 (8192 x 2048: 28.9-39.3 against 24.4-26.6).
   const double nk = (double)N * (double)K;
   const bool rows_ok = M <= 32 || (M <= 64 && (nk <= (double)(1LL << 25) || N >= 65536)) ||
-                       (M <= 96 && N <= 4096 && nk <= (double)(1LL << 24));
+                       (M <= 128 && N <= 4096 && nk <= (double)(1LL << 24)) ||
+                       (M <= 256 && N <= 4096 && nk <= (double)(1LL << 23));
   // K: whole 16-byte chunks (K % 32 == 0), or whole 8-k chunks (K % 8 == 0)
   // where the scale is taken out of the sums (per-channel, groups >= 128):
   // the weight bytes of a chunk that straddles K then meet zero activations

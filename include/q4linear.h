@@ -100,8 +100,9 @@ typedef int32_t q4_status;
 #define Q4_PATH_BWD_F16 4   /* MFMA f16 x f16 -> f32 input gradient */
 #define Q4_PATH_GEMM_F16_SKINNY 5 /* binary16 operands, fp32 sums, from the
                                      few-row kernel (M <= 32; M <= 64 when
-                                     N * K <= 2^25 or N >= 65536; M <= 96 when
-                                     N * K <= 2^24 and N <= 4096; K % 32 == 0,
+                                     N * K <= 2^25 or N >= 65536; with
+                                     N <= 4096 also M <= 128 when N * K <= 2^24
+                                     and M <= 256 when N * K <= 2^23; K % 32 == 0,
                                      or K % 8 == 0 with per-channel scales or
                                      groups >= 128; per-channel or power-of-two
                                      groups >= 32, dword-aligned weight rows):
