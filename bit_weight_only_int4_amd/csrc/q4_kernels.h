@@ -123,7 +123,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group_size)
 hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, void* workspace,
                        hipStream_t s, bool* skinny = nullptr);
 
-// Few-row MFMA GEMM (q4_skinny.hip): 1 <= M <= 256 (by a measured size rule
+// Few-row MFMA GEMM (q4_skinny.hip): 1 <= M <= 1024 (by a measured size rule
 // above 32 rows), K % 32 == 0 (K % 8 == 0 for per-channel scales and groups
 // >= 128), per-channel or power-of-two groups >= 32, dword-aligned weight
 // rows.

@@ -1,4 +1,4 @@
-// q4_skinny.hip -- the plan of the few-row MFMA GEMM (1 <= M <= 256) and its
+// q4_skinny.hip -- the plan of the few-row MFMA GEMM (1 <= M <= 1024) and its
 // launch; the kernel and its design are in q4_skinny_kernels.h.
 #include "q4_kernels.h"
 
@@ -20,19 +20,20 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   // M = 64 on the Llama-3.2-1B projections (N * K <= 2^24: 11.0-17.4 us
   // against 13.7-21.9), the 8B q projection (16.3 against 20.4) and the
   // vocabulary-sized output head (71.6 against 83.5), not on the 8B gate/up
-  // and down projections (31.4 and 32.4 against 27.9 and 29.4); on narrow
-  // N, where the tiled GEMM has few tiles and splits K: at M = 65-128 with
-  // N * K <= 2^24 (2048 x 2048: 9.4-10.1 against 14.7-16.4 us; 2008 x 3000:
-  // 11.8-12.5 against 17.3-19.9; 4096 x 4096: 18.8-21.7 against 20.6-26.0;
-  // 8192 x 2048: 20.4-23.0 against 21.5-26.1), not on 2048 x 8192
-  // (17.7-18.2 against 15.9-17.4 at M = 65-96); at M = 129-256 with
-  // N * K <= 2^23 (2048 x 2048: 12.7-12.9 against 17.7-19.7; 2008 x 3000:
-  // 12.7-14.9 against 21.5-24.6; 1024 x 1024: 7.4-7.7 against 14.0-14.4),
-  // not at 2^24 (8192 x 2048: 28.9-39.3 against 24.4-26.6).
+  // and down projections (31.4 and 32.4 against 27.9 and 29.4); and on
+  // narrow N (<= 4096), where the tiled GEMM has few tiles and splits K,
+  // up to 1024 rows while M * N * K <= 2^31: e.g. K x N = 2048 x 2048 at
+  // M = 65-128 9.4-10.1 against 14.7-16.4 us, at 256 12.8 against 19.7, at
+  // 512 19.2 against 23.7; 8192 x 2048 at M = 97-128 22.2-23.0 against
+  // 23.4-26.1; 2008 x 3000 at 65-320 11.8-16.9 against 17.3-24.7; 1024 x
+  // 1024 at 1024 13.3 against 20.3.  Beyond it the few-row kernel lost
+  // (8192 x 2048 at 160-256: 28.9-39.3 against 24.4-26.6; 2048 x 2048 at
+  // 768: 29.4 against 26.1), as it did on 2048 x 8192 at M = 65-96 (17.7-18.2
+  // against 15.9-17.4).  Inside, the one loss measured: 2048 x 1024 at
+  // M = 1024, 23.3 against 22.5.
   const double nk = (double)N * (double)K;
   const bool rows_ok = M <= 32 || (M <= 64 && (nk <= (double)(1LL << 25) || N >= 65536)) ||
-                       (M <= 128 && N <= 4096 && nk <= (double)(1LL << 24)) ||
-                       (M <= 256 && N <= 4096 && nk <= (double)(1LL << 23));
+                       (M <= 1024 && N <= 4096 && (double)M * nk <= (double)(1LL << 31));
   // K: whole 16-byte chunks (K % 32 == 0), or whole 8-k chunks (K % 8 == 0)
   // where the scale is taken out of the sums (per-channel, groups >= 128):
   // the weight bytes of a chunk that straddles K then meet zero activations

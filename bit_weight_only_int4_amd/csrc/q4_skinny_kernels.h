@@ -1,4 +1,4 @@
-// q4_skinny_kernels.h -- MFMA GEMM for few activation rows (1 <= M <= 256) on
+// q4_skinny_kernels.h -- MFMA GEMM for few activation rows (1 <= M <= 1024) on
 // gfx950: binary16 operands, fp32 accumulation, the arithmetic of the tiled
 // prefill GEMM (q4_gemm.hip):
 //

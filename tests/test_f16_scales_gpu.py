@@ -70,12 +70,12 @@ def _case(M, K, N, gs, *, order="low_first", math="auto", pad=(0, 0, 0, 0), bias
     (16, 8192, 301, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16_skinny"),
     # pipelined GEMM (aligned, even N and pitch), several tiles and ragged M
     (70, 1024, 4136, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
-    (300, 2048, 512, 64, "high_first", "f16", (0, 0, 0, 0), "gemm_f16"),
-    (333, 2048, 700, 0, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
+    (1100, 2048, 512, 64, "high_first", "f16", (0, 0, 0, 0), "gemm_f16"),
+    (1100, 2048, 700, 0, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
     (129, 8192, 2048, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
     # general GEMM: odd N, odd scale pitch, ragged K, small groups
-    (257, 2048, 257, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
-    (257, 2048, 300, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16"),
+    (1100, 2048, 257, 32, "low_first", "f16", (0, 0, 0, 0), "gemm_f16"),
+    (1100, 2048, 300, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16"),
     # few-row GEMM over three row blocks, and K % 32 != 0 with factored scales
     (65, 2048, 300, 32, "high_first", "f16", (0, 0, 1, 0), "gemm_f16_skinny"),
     (65, 2008, 3000, 0, "high_first", "auto", (0, 0, 0, 0), "gemm_f16_skinny"),

@@ -132,7 +132,7 @@ def test_gemm_shapes(M, K, N, gs, order):
     (32, 2048, 300, 0, "gemm_f16_skinny"), (33, 2048, 300, 0, "gemm_f16_skinny"),
     (65, 2048, 300, 0, "gemm_f16_skinny"), (96, 2048, 4096, 128, "gemm_f16_skinny"),
     (97, 2048, 300, 0, "gemm_f16_skinny"), (256, 2048, 300, 0, "gemm_f16_skinny"),
-    (257, 2048, 300, 0, "gemm_f16"), (80, 2048, 8192, 32, "gemm_f16"),
+    (1025, 2048, 300, 0, "gemm_f16"), (80, 2048, 8192, 32, "gemm_f16"),
     (128, 4096, 4096, 128, "gemm_f16_skinny"), (129, 4096, 4096, 128, "gemm_f16"),
     (65, 2008, 3000, 0, "gemm_f16_skinny"), (65, 2008, 3000, 32, "gemm_f16"),
     (2, 2048, 128257, 0, "gemm_f16_skinny"), (7, 2048, 128257, 0, "gemm_f16_skinny"),
@@ -167,10 +167,10 @@ def test_row_pitches_and_unaligned_rows(math):
 # K of every remainder, rows of K / 2 bytes (K % 8 == 0) and padded to a
 # dword, partial last groups, split K, 128 x 256 tiles.
 @pytest.mark.parametrize("M,K,N,gs,qpad,order", [
-    (300, 2008, 3000, 0, 0, "high_first"),   # the 2008 x 3000 shape: K % 64 = 24
-    (300, 1000, 520, 32, 0, "low_first"),    # K % 64 = 40, a last group of 8
-    (300, 2040, 300, 128, 0, "high_first"),  # a last group of 120
-    (300, 200, 3000, 0, 0, "low_first"),     # K % 64 = 8
+    (1100, 2008, 3000, 0, 0, "high_first"),  # the 2008 x 3000 shape: K % 64 = 24
+    (1100, 1000, 520, 32, 0, "low_first"),   # K % 64 = 40, a last group of 8
+    (1100, 2040, 300, 128, 0, "high_first"), # a last group of 120
+    (1100, 200, 3000, 0, 0, "low_first"),    # K % 64 = 8
     (96, 2010, 256, 32, 3, "low_first"),     # K % 8 = 2: rows of 1005 bytes padded to 1008
     (128, 8200, 256, 32, 0, "high_first"),   # split K, the last step in the last split
     (136, 264, 16400, 32, 0, "low_first"),   # 128 x 256 tiles
@@ -189,7 +189,7 @@ def test_pipelined_gemm_bytes_past_k_do_not_reach_the_sum():
     step's copy holds 0x88 there, so the result stays finite."""
     need_gpu()
     rng = np.random.default_rng(8)
-    M, K, N = 300, 2008, 300
+    M, K, N = 1100, 2008, 300
     raw = rng.integers(7, 10, size=(N, K))  # c in {-1, 0, 1}: |c * s| <= 30000
     qw = torch.from_numpy(pack(raw, "low_first"))
     x = torch.from_numpy(rng.uniform(-1, 1, size=(M, K)).astype(np.float32))
@@ -209,11 +209,11 @@ def test_pipelined_gemm_bytes_past_k_do_not_reach_the_sum():
 # a last column quad that is partly past N, M tails, and split-K partials with
 # N % 4 != 0, each with a bias and guard columns around the output.
 @pytest.mark.parametrize("M,K,N,gs,pad_out", [
-    (300, 512, 203, 32, 3),     # no split; element stores (output pitch 206)
+    (1100, 512, 203, 32, 3),    # no split; element stores (output pitch 206)
     (130, 2048, 8202, 64, 2),   # no split; 16-byte stores, last quad ragged, M tail
-    (300, 8192, 130, 128, 0),   # split K; element stores of partials (N % 4 == 2)
-    (300, 4096, 264, 32, 0),    # split K; 16-byte stores of partials
-    (333, 512, 516, 0, 0),      # per-channel scales; 16-byte stores, M tail
+    (1100, 8192, 130, 128, 0),  # split K; element stores of partials (N % 4 == 2)
+    (1100, 4096, 264, 32, 0),   # split K; 16-byte stores of partials
+    (1100, 512, 516, 0, 0),     # per-channel scales; 16-byte stores, M tail
 ])
 def test_pipelined_gemm_output_stores(M, K, N, gs, pad_out):
     need_gpu()
@@ -338,10 +338,10 @@ def test_results_are_deterministic():
 # Repeated calls and graph replays (three kernels per call) must give the
 # same bits, within the oracle's bound.
 @pytest.mark.parametrize("M,K,N,gs,bias", [
-    (512, 2048, 2048, 32, True),    # 64 tiles, 4 splits
+    (513, 2048, 2048, 32, True),    # 80 tiles, 2 splits
     (512, 8192, 2048, 32, False),   # 64 tiles, 4 splits of 32 steps
-    (300, 8192, 130, 128, True),    # 6 tiles, 16 splits, N % 4 != 0 (element path)
-    (300, 4096, 600, 0, True),      # 15 tiles, 8 splits, ragged M and N
+    (1100, 8192, 130, 128, True),   # 18 tiles, 8 splits, N % 4 != 0 (element path)
+    (1100, 4096, 600, 0, True),     # 45 tiles, 4 splits, ragged M and N
 ])
 def test_pipelined_split_k_repeats_and_replays(M, K, N, gs, bias):
     need_gpu()

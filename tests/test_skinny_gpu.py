@@ -1,4 +1,4 @@
-"""GPU parity of the few-row MFMA GEMM (M <= 256) against the fp64 oracle,
+"""GPU parity of the few-row MFMA GEMM (M <= 1024) against the fp64 oracle,
 through the C ABI, and the boundary between it and the tiled GEMM.
 
 The kernel's plan depends on the sizes alone, so the shapes below are
@@ -14,7 +14,7 @@ beside each case):
     reduce;
   * staging of the activations in several rounds (M * K / 8 > 2048);
   * more than 32 rows: row blocks of 32 in separate workgroups (two to
-    eight);
+    32);
   * ragged N, both nibble orders, per-channel and grouped scales (32, 128),
     fp32 and binary16 scales, bias on and off, row pitches, and a NaN-poisoned
     output with guard rows and columns.
@@ -40,19 +40,19 @@ def inputs(M, K, N, gs, order="low_first", bias=False, seed=0):
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 24, 32, 33, 48, 64, 65, 96, 97, 128, 200,
-                               256, 257])
+                               257, 1024, 1025])
 @pytest.mark.parametrize("order", ["low_first", "high_first"])
 @pytest.mark.parametrize("gs", [0, 32, 128])
 def test_rows_around_the_boundary(M, order, gs):
-    """M <= 256 runs the skinny kernel here (N * K <= 2^23 and N <= 4096;
-    above 32 rows in row blocks of 32), M >= 257 the tiled GEMM; N = 1000 is
-    ragged against 16- and 32-column blocks (wk = 8 here)."""
+    """M <= 1024 runs the skinny kernel here (M * N * K <= 2^31 and
+    N <= 4096; above 32 rows in row blocks of 32), M >= 1025 the tiled GEMM;
+    N = 1000 is ragged against 16- and 32-column blocks (wk = 8 here)."""
     need_gpu()
     K, N = 2048, 1000
     x, qw, s, bias = inputs(M, K, N, gs, order=order, bias=(M % 2 == 1), seed=M * 31 + gs)
     _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order=order, math="f16",
                             label="skinny-boundary")
-    assert path == (SKINNY if M <= 256 else "gemm_f16")
+    assert path == (SKINNY if M <= 1024 else "gemm_f16")
 
 
 @pytest.mark.parametrize("M,K,N,gs,expect", [
@@ -66,9 +66,11 @@ def test_rows_around_the_boundary(M, order, gs):
     (90, 8192, 2048, 32, SKINNY),            # three row blocks, K split over 4 + reduce
     (96, 4096, 4096, 0, SKINNY),             # N * K = 2^24, N = 4096
     (70, 2048, 4097, 0, "gemm_f16"),         # N > 4096 above 64 rows: the tiled GEMM
-    (80, 4104, 4096, 0, "gemm_f16"),         # N * K > 2^24 above 64 rows
+    (140, 4104, 4096, 0, "gemm_f16"),        # M * N * K > 2^31
     (128, 4096, 4096, 0, SKINNY),            # four row blocks, N * K = 2^24
-    (129, 4096, 4096, 0, "gemm_f16"),        # N * K > 2^23 above 128 rows
+    (129, 4096, 4096, 0, "gemm_f16"),        # M * N * K > 2^31
+    (512, 2048, 2048, 32, SKINNY),           # 16 row blocks, M * N * K = 2^31
+    (513, 2048, 2048, 32, "gemm_f16"),
     (256, 2048, 4096, 128, SKINNY),          # eight row blocks, N * K = 2^23
     (250, 8192, 1000, 32, SKINNY),           # eight row blocks, the last of 26 rows, K split
 ])
