@@ -238,6 +238,8 @@ def test_repeat_calls_are_bit_identical():
     (96, 2040, 3000, 128, "low_first"),  # K % 32 = 24, three row blocks
     (16, 8200, 300, 0, "high_first"),    # K split over workgroups, the straddle in the last slice
     (3, 136, 70, 0, "low_first"),        # two steps, the second of 8 k
+    (300, 2008, 3000, 0, "low_first"),   # ten row blocks, the last of 12 rows
+    (700, 1000, 2000, 128, "high_first"),  # 22 row blocks, groups of 128
 ])
 def test_k_not_a_multiple_of_32(M, K, N, gs, order):
     need_gpu()
