@@ -3,8 +3,9 @@ C ABI: every kernel the automatic choice (or a forced math) picks, with
 ragged M, N and K, group sizes of every kind, both nibble orders, row
 pitches, bias on and off, NaN-poisoned outputs with guard rows and columns.
 The shapes are drawn to fall around the kernels' boundaries: 1-4 rows (the
-fp32 GEMVs), up to 32, 64 and 96 rows (the few-row kernel's row blocks),
-above 96 (the tiled GEMM), K a multiple of 32, of 8, even or odd.
+fp32 GEMVs), up to 32, 64 and 96 rows and beyond (the few-row kernel's row
+blocks, up to 1024 rows on small weights), the tiled GEMM above, K a
+multiple of 32, of 8, even or odd.
 The bar is the path's own: 1e-5 for the fp32 GEMV, 2e-3 for binary16
 operands, normalised by sum_k |x * w|.
 """
@@ -20,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def draw(i):
     rng = np.random.default_rng(1000 + i)
     M = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 17, 24, 31, 32, 33, 40, 48, 63, 64, 65,
-                        70, 80, 95, 96, 97, 100, 128, 129]))
+                        70, 80, 95, 96, 97, 100, 128, 129, 200, 300, 512, 700]))
     kind = int(rng.integers(0, 4))
     if kind == 0:
         K = 32 * int(rng.integers(4, 130))       # whole 16-byte chunks
