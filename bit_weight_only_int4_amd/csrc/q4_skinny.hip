@@ -21,8 +21,10 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   // against 13.7-21.9), the 8B q projection (16.3 against 20.4) and the
   // vocabulary-sized output head (71.6 against 83.5), not on the 8B gate/up
   // and down projections (31.4 and 32.4 against 27.9 and 29.4); and on
-  // narrow N (<= 4096), where the tiled GEMM has few tiles and splits K,
-  // up to 1024 rows while M * N * K <= 2^31: e.g. K x N = 2048 x 2048 at
+  // narrow N (<= 4096) with N * K <= 2^24, where the tiled GEMM has few
+  // tiles and splits K, up to 1024 rows while M * N * K <= 2^31 (larger
+  // weights lost even at 33-40 rows: 14336 x 4096 31.4-32.0 against
+  // 27.7-28.4 us, 12288 x 4096 29.0 against 26.4): e.g. K x N = 2048 x 2048 at
   // M = 65-128 9.4-10.1 against 14.7-16.4 us, at 256 12.8 against 19.7, at
   // 512 19.2 against 23.7; 8192 x 2048 at M = 97-128 22.2-23.0 against
   // 23.4-26.1; 2008 x 3000 at 65-320 11.8-16.9 against 17.3-24.7; 1024 x
@@ -33,7 +35,8 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   // M = 1024, 23.3 against 22.5.
   const double nk = (double)N * (double)K;
   const bool rows_ok = M <= 32 || (M <= 64 && (nk <= (double)(1LL << 25) || N >= 65536)) ||
-                       (M <= 1024 && N <= 4096 && (double)M * nk <= (double)(1LL << 31));
+                       (M <= 1024 && N <= 4096 && nk <= (double)(1LL << 24) &&
+                        (double)M * nk <= (double)(1LL << 31));
   // K: whole 16-byte chunks (K % 32 == 0), or whole 8-k chunks (K % 8 == 0)
   // where the scale is taken out of the sums (per-channel, groups >= 128):
   // the weight bytes of a chunk that straddles K then meet zero activations

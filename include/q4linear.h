@@ -101,8 +101,9 @@ typedef int32_t q4_status;
 #define Q4_PATH_GEMM_F16_SKINNY 5 /* binary16 operands, fp32 sums, from the
                                      few-row kernel (M <= 32; M <= 64 when
                                      N * K <= 2^25 or N >= 65536; with
-                                     N <= 4096 also M <= 1024 when
-                                     M * N * K <= 2^31; K % 32 == 0,
+                                     N <= 4096 and N * K <= 2^24 also
+                                     M <= 1024 when M * N * K <= 2^31;
+                                     K % 32 == 0,
                                      or K % 8 == 0 with per-channel scales or
                                      groups >= 128; per-channel or power-of-two
                                      groups >= 32, dword-aligned weight rows):

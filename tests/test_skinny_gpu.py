@@ -44,8 +44,9 @@ def inputs(M, K, N, gs, order="low_first", bias=False, seed=0):
 @pytest.mark.parametrize("order", ["low_first", "high_first"])
 @pytest.mark.parametrize("gs", [0, 32, 128])
 def test_rows_around_the_boundary(M, order, gs):
-    """M <= 1024 runs the skinny kernel here (M * N * K <= 2^31 and
-    N <= 4096; above 32 rows in row blocks of 32), M >= 1025 the tiled GEMM;
+    """M <= 1024 runs the skinny kernel here (M * N * K <= 2^31,
+    N * K <= 2^24, N <= 4096; above 32 rows in row blocks of 32), M >= 1025
+    the tiled GEMM;
     N = 1000 is ragged against 16- and 32-column blocks (wk = 8 here)."""
     need_gpu()
     K, N = 2048, 1000
@@ -69,6 +70,7 @@ def test_rows_around_the_boundary(M, order, gs):
     (140, 4104, 4096, 0, "gemm_f16"),        # M * N * K > 2^31
     (128, 4096, 4096, 0, SKINNY),            # four row blocks, N * K = 2^24
     (129, 4096, 4096, 0, "gemm_f16"),        # M * N * K > 2^31
+    (36, 14336, 4096, 128, "gemm_f16"),      # N * K > 2^25 above 32 rows
     (512, 2048, 2048, 32, SKINNY),           # 16 row blocks, M * N * K = 2^31
     (513, 2048, 2048, 32, "gemm_f16"),
     (256, 2048, 4096, 128, SKINNY),          # eight row blocks, N * K = 2^23
