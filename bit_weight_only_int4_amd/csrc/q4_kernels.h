@@ -124,9 +124,8 @@ hipError_t launch_gemm(const GemmParams& p, int order, bool qa4, void* workspace
                        hipStream_t s, bool* skinny = nullptr);
 
 // Few-row MFMA GEMM (q4_skinny.hip): 1 <= M <= 1024 (by a measured size rule
-// above 32 rows), K % 32 == 0 (K % 8 == 0 for per-channel scales and groups
-// >= 128), per-channel or power-of-two groups >= 32, dword-aligned weight
-// rows.
+// above 32 rows), K % 8 == 0, per-channel or power-of-two groups >= 32,
+// dword-aligned weight rows.
 struct SkinnyPlan {
   bool ok;          // the sizes are the kernel's
   int mz;           // row blocks (of mrows rows) handled by separate workgroups

@@ -37,11 +37,11 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t group_size) {
   const bool rows_ok = M <= 32 || (M <= 64 && (nk <= (double)(1LL << 25) || N >= 65536)) ||
                        (M <= 1024 && N <= 4096 && nk <= (double)(1LL << 24) &&
                         (double)M * nk <= (double)(1LL << 31));
-  // K: whole 16-byte chunks (K % 32 == 0), or whole 8-k chunks (K % 8 == 0)
-  // where the scale is taken out of the sums (per-channel, groups >= 128):
-  // the weight bytes of a chunk that straddles K then meet zero activations
-  // as exact codes, whatever they hold (see the kernel)
-  const bool kok = K % 32 == 0 || (K % 8 == 0 && (perch || (pow2 && group_size >= 128)));
+  // K: whole 8-k chunks (K % 8 == 0).  The weight bytes past K of the
+  // 32-k chunk that straddles K meet zero activations as exact codes where
+  // the scale is taken out of the sums (per-channel, groups >= 128), and get
+  // a zero scale otherwise (see the kernel)
+  const bool kok = K % 8 == 0;
   pl.ok = M >= 1 && rows_ok && N >= 1 && K >= SK_STEP && kok && (perch || pow2) &&
           K <= ((int64_t)1 << 24);
   if (!pl.ok) return pl;

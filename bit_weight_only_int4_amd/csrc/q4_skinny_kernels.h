@@ -110,8 +110,10 @@ __device__ __forceinline__ float sk_scale(__amdgpu_buffer_rsrc_t r, uint32_t off
 //               operand;
 //   SC_STEP:    power-of-two groups >= 128: B = c (exact), the step's MFMA
 //               sum times s (one fp32 multiply-add into the accumulator);
-//   SC_CHANNEL: per-channel scales: B = c, the whole sum times s at the end.
-enum SkScale : int { SC_ELEM = 0, SC_STEP = 1, SC_CHANNEL = 2 };
+//   SC_CHANNEL: per-channel scales: B = c, the whole sum times s at the end;
+//   SC_ELEM_KT: SC_ELEM with K % 32 != 0 (K % 8 == 0): the 32-k chunk that
+//               straddles K gets a zero scale for its 8-k words past K.
+enum SkScale : int { SC_ELEM = 0, SC_STEP = 1, SC_CHANNEL = 2, SC_ELEM_KT = 3 };
 
 // MB: 16-row MFMA blocks per row block (1: <= 16 rows, 2: <= 32).  NI: 16-column blocks
 // per wave (2 or 4: 32 or 64 columns, NI 16-byte weight loads per lane and
@@ -301,12 +303,14 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         a[t][mb] = *reinterpret_cast<const h8*>(ab + aoff[mb][t]);
-    if constexpr (SC == SC_ELEM) {
+    if constexpr (SC == SC_ELEM || SC == SC_ELEM_KT) {
       // chunks past K (the last step of a K that is not a multiple of 128)
-      // get a zero scale, so that whatever bytes they read give w = 0 (the
-      // plan takes this mode only with K % 32 == 0: a lane's 32-k chunk lies
-      // wholly inside K or wholly past it)
-      const bool pastk = kz0 + SK_STEP * sidx + 32 * g >= K;
+      // get a zero scale, so that whatever bytes they read give w = 0; with
+      // K % 32 != 0 so do the 8-k words past K of the chunk that straddles
+      // it (bytes of the row pitch, of the next row, or zeros past the
+      // array: a code times a zero scale is 0 whatever the code)
+      const int64_t kc = kz0 + SK_STEP * sidx + 32 * g;  // the lane's chunk
+      const bool pastk = kc >= K;
       h2 s16[NI];
 #pragma unroll
       for (int u = 0; u < NI; ++u) s16[u] = splat_f16(pastk ? 0.0f : sl.s[u]);
@@ -316,9 +320,13 @@ gemm_skinny_kernel(const GemmParams p, const SkinnyPlan pl) {
         for (int u = 0; u < NI; ++u) {
           h2 c[4];
           unpack_word(sl.q[u][t], mg, c);
+          h2 su = s16[u];
+          if constexpr (SC == SC_ELEM_KT) {
+            if (kc + 8 * t >= K) su = h2{(_Float16)0.0f, (_Float16)0.0f};
+          }
           h2 d[4];
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) d[pp] = dequant_pair_f16(c[pp], s16[u]);
+          for (int pp = 0; pp < 4; ++pp) d[pp] = dequant_pair_f16(c[pp], su);
           const h8 bv = h8{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
@@ -488,7 +496,9 @@ template <int ORDER>
 hipError_t launch_skinny_kernels(const GemmParams& p, const SkinnyPlan& pl, bool perch,
                                  hipStream_t s) {
   if (perch) return launch_sk_s<ORDER, SC_CHANNEL>(p, pl, s);
-  return p.log2_gs >= 7 ? launch_sk_s<ORDER, SC_STEP>(p, pl, s) : launch_sk_s<ORDER, SC_ELEM>(p, pl, s);
+  if (p.log2_gs >= 7) return launch_sk_s<ORDER, SC_STEP>(p, pl, s);
+  return p.K % 32 == 0 ? launch_sk_s<ORDER, SC_ELEM>(p, pl, s)
+                       : launch_sk_s<ORDER, SC_ELEM_KT>(p, pl, s);
 }
 
 }  // namespace q4

@@ -103,10 +103,9 @@ typedef int32_t q4_status;
                                      N * K <= 2^25 or N >= 65536; with
                                      N <= 4096 and N * K <= 2^24 also
                                      M <= 1024 when M * N * K <= 2^31;
-                                     K % 32 == 0, or K % 8 == 0 with
-                                     per-channel scales or groups >= 128;
-                                     per-channel or power-of-two groups
-                                     >= 32; dword-aligned weight rows): one
+                                     K % 8 == 0; per-channel or
+                                     power-of-two groups >= 32;
+                                     dword-aligned weight rows): one
                                      launch, plus the split-K reduce where a
                                      row block's binary16 activations exceed
                                      LDS or narrow N over deep K leaves CUs

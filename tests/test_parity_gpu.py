@@ -134,11 +134,12 @@ def test_gemm_shapes(M, K, N, gs, order):
     (97, 2048, 300, 0, "gemm_f16_skinny"), (256, 2048, 300, 0, "gemm_f16_skinny"),
     (1025, 2048, 300, 0, "gemm_f16"), (80, 2048, 8192, 32, "gemm_f16"),
     (128, 4096, 4096, 128, "gemm_f16_skinny"), (129, 4096, 4096, 128, "gemm_f16"),
-    (65, 2008, 3000, 0, "gemm_f16_skinny"), (65, 2008, 3000, 32, "gemm_f16"),
+    (65, 2008, 3000, 0, "gemm_f16_skinny"), (65, 2008, 3000, 32, "gemm_f16_skinny"),
+    (65, 2010, 3000, 32, "gemm_f16"),
     (2, 2048, 128257, 0, "gemm_f16_skinny"), (7, 2048, 128257, 0, "gemm_f16_skinny"),
     (2, 14336, 4096, 128, "gemm_f16_skinny"), (3, 4096, 14336, 128, "gemm_f16_skinny"),
     (4, 2048, 300, 8, "gemm_f16"), (4, 2040, 300, 32, "gemv_f32"),
-    (20, 2040, 300, 32, "gemm_f16"), (9, 2040, 2048, 32, "gemv_f32"),
+    (20, 2040, 300, 32, "gemm_f16_skinny"), (9, 2040, 2048, 32, "gemv_f32"),
 ])
 def test_auto_regime(M, K, N, gs, expect):
     """The automatic choice of kernel, and its parity at that kernel's bar."""
@@ -172,7 +173,7 @@ def test_row_pitches_and_unaligned_rows(math):
     (1100, 2040, 300, 128, 0, "high_first"), # a last group of 120
     (1100, 200, 3000, 0, 0, "low_first"),    # K % 64 = 8
     (96, 2010, 256, 32, 3, "low_first"),     # K % 8 = 2: rows of 1005 bytes padded to 1008
-    (128, 8200, 256, 32, 0, "high_first"),   # split K, the last step in the last split
+    (1100, 8200, 256, 32, 0, "high_first"),  # split K, the last step in the last split
     (136, 264, 16400, 32, 0, "low_first"),   # 128 x 256 tiles
 ])
 def test_pipelined_gemm_k_tail(M, K, N, gs, qpad, order):

@@ -133,14 +133,14 @@ def test_unaligned_weight_rows_take_the_tiled_kernel():
 @pytest.mark.parametrize("M,K,gs", [(8, 2056, 32), (8, 2056, 64), (8, 2048, 64), (8, 2048, 48),
                                     (8, 2048, 16), (8, 2052, 0)])
 def test_other_shapes_take_the_tiled_kernel(M, K, gs):
-    """K % 32 != 0 with groups of 32 or 64 (the scale multiplies each
-    weight), K % 8 != 0, and groups that are not powers of two >= 32 are the
-    tiled kernel's."""
+    """K % 8 != 0 and groups that are not powers of two >= 32 are the
+    tiled kernel's; K % 32 != 0 with groups of 32 or 64 stays on the few-row
+    kernel (a zero scale for the words past K)."""
     need_gpu()
     x, qw, s, bias = inputs(M, K, 200, gs, seed=19)
     _, path, _ = check_case(x, qw, s, bias, K=K, gs=gs, order="low_first", math="f16",
                             label="skinny-other")
-    assert path == (SKINNY if (gs == 64 and K % 32 == 0) else "gemm_f16")
+    assert path == (SKINNY if (gs in (32, 64) and K % 8 == 0) else "gemm_f16")
 
 
 @pytest.mark.parametrize("M,gs", [(7, 0), (24, 32), (5, 128)])
@@ -241,6 +241,12 @@ def test_repeat_calls_are_bit_identical():
     (16, 8200, 300, 0, "high_first"),    # K split over workgroups, the straddle in the last slice
     (3, 136, 70, 0, "low_first"),        # two steps, the second of 8 k
     (300, 2008, 3000, 0, "low_first"),   # ten row blocks, the last of 12 rows
+    (7, 2008, 300, 32, "high_first"),    # groups of 32: the straddling chunk's last
+                                         # word past K gets a zero scale
+    (33, 1000, 513, 64, "low_first"),    # groups of 64, a last group of 40
+    (5, 2056, 200, 32, "low_first"),     # K % 32 = 8: three words of the chunk past K
+    (96, 2040, 3000, 32, "high_first"),  # K % 32 = 24, three row blocks
+    (16, 8200, 300, 32, "low_first"),    # K split over workgroups
     (700, 1000, 2000, 128, "high_first"),  # 22 row blocks, groups of 128
 ])
 def test_k_not_a_multiple_of_32(M, K, N, gs, order):
@@ -251,7 +257,7 @@ def test_k_not_a_multiple_of_32(M, K, N, gs, order):
     assert path == SKINNY
 
 
-@pytest.mark.parametrize("M,gs", [(5, 0), (40, 128)])
+@pytest.mark.parametrize("M,gs", [(5, 0), (40, 128), (7, 32), (33, 64)])
 def test_k_not_a_multiple_of_32_bytes_past_k(M, gs):
     """Row pitch padding of 0xFF (code 15) past K = 2008 and scales of 30000:
     the straddling chunk's bytes past K still add nothing, and nothing turns
